@@ -1,0 +1,141 @@
+/*
+ * tl.h — C ABI of the ternary g128 linear-layer library for MI355X (gfx950).
+ *
+ * The layer computes  y = dequant(codes, scales) · R(x)  where
+ *   - codes are ternary weights in {-1, 0, +1} with one binary16 scale per 128
+ *     consecutive weights of a row ("ternary g128"); source: page "A 27-billion
+ *     model that fits in 8.6 GB" (news.ditty.ir), paragraph 2, and page
+ *     "Ternary Bonsai 2 27B: 27B-модель в 5,9 ГБ" (ai4coding.ru), section
+ *     "Что такое тернарная модель";
+ *   - R is the signed block-Hadamard rotation over 1024-wide blocks that was
+ *     folded into the weights and must be applied to the activations at run
+ *     time; source: the Persian page, paragraphs 2 and 3, and page "OpenBonsai"
+ *     (openbonsai.org), section "How it works", step 1;
+ *   - the codes are stored in one of two byte packings of the same weights, a
+ *     dense one with 5 trits per byte and one with a 2-bit slot per weight;
+ *     source: the Persian page, paragraph 5.
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense row-major device buffers owned by the caller; the
+ *     library never allocates, frees or retains them.
+ *   - binary16 data is passed as uint16_t (bit patterns).
+ *   - Every call validates its arguments first.  On a validation failure it
+ *     returns the status and launches nothing, so outputs are untouched.
+ *   - On success the work is enqueued on `stream` (0 = the null stream) and the
+ *     call returns TL_OK without synchronising.  A launch failure returns
+ *     TL_ERR_LAUNCH and tl_last_error() gives the HIP error text (per thread).
+ *   - The library keeps no state between calls apart from that per-thread
+ *     error text; calls from several threads are safe.
+ *
+ * Formats (bit-exact; defined here, since the pages give no byte layout)
+ *   digit d = code + 1, in {0, 1, 2}.
+ *   TL_FMT_TRIT5: each row holds K/128 groups of 26 bytes (row stride 26*K/128
+ *     bytes).  Byte j < 25 of a group = sum_{i<5} d[5j+i] * 3^i (values 0..242,
+ *     first digit least significant).  Byte 25 = d[125] + 3 d[126] + 9 d[127]
+ *     + 27 + 81: the two pad digits are 1 (code 0), values 108..134.
+ *     1.625 code bits + 0.125 scale bits = 1.75 bits per weight.
+ *   TL_FMT_SLOT2: each row holds K/4 bytes; bits 2i..2i+1 of byte j hold
+ *     d[4j+i].  2.125 bits per weight with the scales.
+ *   Scales: binary16 [N, K/128]; weight (n, k) = code * scales[n, k/128].
+ *   Signs: int8 [K] of +1/-1; block b of the rotation uses signs[1024b .. +1023].
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TL_API __attribute__((visibility("default")))
+#else
+#define TL_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TL_OK = 0,
+    TL_ERR_NULL = 1,     /* a required pointer is NULL                          */
+    TL_ERR_SHAPE = 2,    /* a size is out of range (see each call)             */
+    TL_ERR_FORMAT = 3,   /* unknown packing format                             */
+    TL_ERR_ALIGN = 4,    /* a pointer is not 16-byte aligned                   */
+    TL_ERR_ALIAS = 5,    /* an output overlaps an input it must not overlap    */
+    TL_ERR_LAUNCH = 6,   /* the HIP launch failed; see tl_last_error()         */
+    TL_ERR_DTYPE = 7     /* unknown output dtype                               */
+} tl_status;
+
+enum { TL_FMT_TRIT5 = 0, TL_FMT_SLOT2 = 1 };
+enum { TL_F32 = 0, TL_F16 = 1 };
+
+#define TL_BLOCK 1024      /* Hadamard block width                 */
+#define TL_GROUP 128       /* weights per scale                    */
+#define TL_MAX_K (1 << 20) /* largest K any call accepts           */
+
+/* Bytes of the packed code array for an N x K weight in format `fmt`
+ * (scales not included).  Host only.  Returns -1 when N < 1, K < 128,
+ * K % 128 != 0 or fmt is unknown. */
+TL_API int64_t tl_packed_bytes(int64_t N, int64_t K, int32_t fmt);
+
+/* Pack ternary codes.  codes: int8 [N, K] (device); packed: uint8 of
+ * tl_packed_bytes(N, K, fmt) bytes (device).  Requires 1 <= N <= 2^24,
+ * K >= 128, K % 128 == 0, K <= TL_MAX_K, N * K <= 2^36.  codes and packed
+ * must be 16-byte aligned, bad_count 4-byte aligned.  A code outside {-1, 0, 1} is packed as 0
+ * and counted: when bad_count (device int32, may be NULL) is given, the
+ * number of such codes is ADDED to *bad_count (the caller clears it).
+ * packed must not overlap codes.  Bit-exact with the format above. */
+TL_API tl_status tl_pack(const int8_t* codes, int64_t N, int64_t K, int32_t fmt,
+                  uint8_t* packed, int32_t* bad_count, hipStream_t stream);
+
+/* Unpack to int8 codes [N, K] (device).  Same shape rules as tl_pack.
+ * Bytes that are not valid encodings give unspecified codes in {-1, 0, 1}. */
+TL_API tl_status tl_unpack(const uint8_t* packed, int64_t N, int64_t K, int32_t fmt,
+                    int8_t* codes, hipStream_t stream);
+
+/* Signed block-Hadamard rotation of the rows of x:
+ *   x_rot[m, 1024b + i] = (1/32) sum_j H[i, j] signs[1024b + j] x[m, 1024b + j]
+ * with H the Sylvester Hadamard matrix of order 1024 (H[i,j] = (-1)^popcount(i&j)).
+ * x, x_rot: binary16 [M, K]; signs: int8 [K].  Computed in fp32, rounded to
+ * binary16 to nearest even.  Requires 1 <= M <= 2^24, K >= 1024,
+ * K % 1024 == 0, K <= TL_MAX_K, M * K <= 2^36.  A negative sign byte means -1,
+ * any other value +1.  x_rot may equal x (in place) but must not otherwise
+ * overlap x or signs.  Source: the Persian page, paragraphs 2 and 3. */
+TL_API tl_status tl_hadamard_rotate(const uint16_t* x, const int8_t* signs, int64_t M, int64_t K,
+                             uint16_t* x_rot, hipStream_t stream);
+
+/* Ternary linear on already rotated activations (decode shapes):
+ *   y[m, n] = sum_k x_rot[m, k] * code[n, k] * scales[n, k/128]
+ * packed: [N, ...] in format fmt; scales: binary16 [N, K/128]; x_rot: binary16
+ * [M, K]; y: [M, N] of y_dtype (TL_F32, or TL_F16 rounded to nearest even).
+ * Products are exact, sums in fp32, and the result does not depend on the
+ * launch (bitwise deterministic).  Requires 1 <= M, N <= 2^24, K >= 1024,
+ * K % 1024 == 0, K <= TL_MAX_K, and M*K, N*K, M*N <= 2^36.  Tuned for
+ * M <= 16; any M is accepted.  y must
+ * not overlap any input.  Multiply-accumulate with ternary weights is
+ * additions and subtractions (ai4coding.ru page, section "Что такое тернарная
+ * модель"). */
+TL_API tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                  const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
+                  void* y, int32_t y_dtype, hipStream_t stream);
+
+/* Same operation and argument rules as tl_gemv, tuned for prefill (M >= 64):
+ * weight tiles are expanded to exact binary16 (code * scale) on chip and fed
+ * to fp16 matrix-core instructions with fp32 accumulation.  Prompt processing
+ * is where the pages place the practical bottleneck on slower chips (Persian
+ * page, paragraph 4). */
+TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                  const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
+                  void* y, int32_t y_dtype, hipStream_t stream);
+
+/* Static name of a status code ("TL_OK", ...). */
+TL_API const char* tl_status_str(tl_status status);
+
+/* Text of the last TL_ERR_LAUNCH on the calling thread ("" if none). */
+TL_API const char* tl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TL_H */

@@ -1,0 +1,197 @@
+"""Python binding of libtl (ternary g128 linear layer with a signed
+block-Hadamard rotation, MI355X / gfx950).
+
+Argument marshalling only: every function checks dtype, shape, device and
+contiguity of torch tensors, then passes raw device pointers and torch's
+current HIP stream to the C ABI declared in include/tl.h.  All computation runs
+in the library's HIP kernels; there is no fallback path.  A missing library
+raises at first use.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtl.so")
+
+FMT_TRIT5 = 0
+FMT_SLOT2 = 1
+TL_F32 = 0
+TL_F16 = 1
+BLOCK = 1024
+GROUP = 128
+
+_STATUS = {0: "TL_OK", 1: "TL_ERR_NULL", 2: "TL_ERR_SHAPE", 3: "TL_ERR_FORMAT",
+           4: "TL_ERR_ALIGN", 5: "TL_ERR_ALIAS", 6: "TL_ERR_LAUNCH", 7: "TL_ERR_DTYPE"}
+
+_lib = None
+
+
+class TLError(RuntimeError):
+    def __init__(self, call: str, status: int, detail: str = ""):
+        self.status = status
+        self.status_name = _STATUS.get(status, f"status {status}")
+        msg = f"{call} failed: {self.status_name}"
+        if detail:
+            msg += f" ({detail})"
+        super().__init__(msg)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtl.so (built by ``python -m tl_hadamard_rotate_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m tl_hadamard_rotate_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        sig = {
+            "tl_packed_bytes": (i64, [i64, i64, i32]),
+            "tl_pack": (i32, [p, i64, i64, i32, p, p, p]),
+            "tl_unpack": (i32, [p, i64, i64, i32, p, p]),
+            "tl_hadamard_rotate": (i32, [p, p, i64, i64, p, p]),
+            "tl_gemv": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
+            "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
+            "tl_status_str": (ctypes.c_char_p, [i32]),
+            "tl_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(call: str, status: int) -> None:
+    if status != 0:
+        detail = lib().tl_last_error().decode() if status == 6 else ""
+        raise TLError(call, status, detail)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int | None = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def packed_bytes(n: int, k: int, fmt: int) -> int:
+    return int(lib().tl_packed_bytes(n, k, fmt))
+
+
+def pack(codes: torch.Tensor, fmt: int, bad_count: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 codes [N, K] -> uint8 packed [N, row_bytes] (see include/tl.h)."""
+    _need(codes, "codes", torch.int8, 2)
+    if bad_count is not None:
+        _need(bad_count, "bad_count", torch.int32)
+    n, k = codes.shape
+    nbytes = packed_bytes(n, k, fmt)
+    if nbytes < 0:
+        raise TLError("tl_pack", 2)
+    out = torch.empty((n, nbytes // n), dtype=torch.uint8, device=codes.device)
+    _check("tl_pack", lib().tl_pack(_ptr(codes), n, k, fmt, _ptr(out), _ptr(bad_count),
+                                    _stream(codes)))
+    return out
+
+
+def unpack(packed: torch.Tensor, k: int, fmt: int) -> torch.Tensor:
+    _need(packed, "packed", torch.uint8, 2)
+    n = packed.shape[0]
+    out = torch.empty((n, k), dtype=torch.int8, device=packed.device)
+    if packed.numel() != packed_bytes(n, k, fmt):
+        raise ValueError("packed size does not match K and the format")
+    _check("tl_unpack", lib().tl_unpack(_ptr(packed), n, k, fmt, _ptr(out), _stream(packed)))
+    return out
+
+
+def hadamard_rotate(x: torch.Tensor, signs: torch.Tensor,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """Signed 1024-block Hadamard rotation of the rows of fp16 x [M, K]."""
+    _need(x, "x", torch.float16, 2)
+    _need(signs, "signs", torch.int8, 1)
+    m, k = x.shape
+    if signs.shape[0] != k:
+        raise ValueError("signs must have K entries")
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", torch.float16, 2)
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    _check("tl_hadamard_rotate",
+           lib().tl_hadamard_rotate(_ptr(x), _ptr(signs), m, k, _ptr(out), _stream(x)))
+    return out
+
+
+def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out):
+    _need(packed, "packed", torch.uint8, 2)
+    _need(scales, "scales", torch.float16, 2)
+    _need(x_rot, "x_rot", torch.float16, 2)
+    m, k = x_rot.shape
+    n = packed.shape[0]
+    if scales.shape != (n, k // GROUP):
+        raise ValueError(f"scales must be [N, K/128] = {(n, k // GROUP)}, got {tuple(scales.shape)}")
+    if packed.numel() != packed_bytes(n, k, fmt):
+        raise ValueError("packed size does not match N, K and the format")
+    if out_dtype not in (torch.float32, torch.float16):
+        raise TypeError("out_dtype must be float32 or float16")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x_rot.device)
+    else:
+        _need(out, "out", out_dtype, 2)
+        if out.shape != (m, n):
+            raise ValueError("out must be [M, N]")
+    yd = TL_F32 if out_dtype == torch.float32 else TL_F16
+    fn = getattr(lib(), call)
+    _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
+                    _stream(x_rot)))
+    return out
+
+
+def gemv(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """y[M, N] = x_rot . dequant(codes, scales)^T, decode-shaped (M <= 16)."""
+    return _linear("tl_gemv", packed, scales, fmt, x_rot, out_dtype, out)
+
+
+def gemm(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """Same as ``gemv``, prefill-shaped (large M)."""
+    return _linear("tl_gemm", packed, scales, fmt, x_rot, out_dtype, out)
+
+
+class TernaryLinear:
+    """A ternary g128 linear layer whose weights carry the folded rotation.
+
+    ``forward`` always rotates its input first: skipping the runtime rotation
+    gives wrong output without any error (page "A 27-billion model that fits
+    in 8.6 GB", paragraph 3), so it is not optional here."""
+
+    def __init__(self, packed, scales, fmt, signs, prefill_threshold: int = 64):
+        self.packed, self.scales, self.fmt, self.signs = packed, scales, fmt, signs
+        self.prefill_threshold = prefill_threshold
+
+    def forward(self, x: torch.Tensor, out_dtype=torch.float32) -> torch.Tensor:
+        x_rot = hadamard_rotate(x, self.signs)
+        if x.shape[0] >= self.prefill_threshold:
+            return gemm(self.packed, self.scales, self.fmt, x_rot, out_dtype)
+        return gemv(self.packed, self.scales, self.fmt, x_rot, out_dtype)
+
+    __call__ = forward

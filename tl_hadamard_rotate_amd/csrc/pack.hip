@@ -1,0 +1,143 @@
+// Packing of ternary codes into the two byte formats, and the reverse.
+// Formats: 5 trits per byte in base 3 (26 bytes per 128-group) and one 2-bit
+// slot per weight; both hold digit d = code + 1.  The two packings carry the
+// same weights and differ only in layout (page "A 27-billion model that fits
+// in 8.6 GB", paragraph 5).  Bit-exact integer work; offline, once per weight.
+#include "tl_internal.h"
+
+namespace tl {
+namespace {
+
+constexpr int kThreads = 256;
+
+// digit of one code; codes outside {-1,0,1} become digit 1 (code 0) and are counted
+__device__ __forceinline__ uint32_t code_digit(int8_t c, uint32_t& bad) {
+    uint32_t ok = (c >= -1) & (c <= 1);
+    bad += ok ^ 1u;
+    return ok ? uint32_t(c + 1) : 1u;
+}
+
+// One thread per output byte of a 26-byte group: byte j < 25 takes codes
+// 5j..5j+4, byte 25 takes codes 125..127 and two pad digits of 1.
+__global__ __launch_bounds__(kThreads) void pack_trit5_kernel(
+    const int8_t* __restrict__ codes, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int32_t* __restrict__ bad_count) {
+    const int64_t row_bytes = (k / kGroup) * kTrit5GroupBytes;
+    const int64_t total = n * row_bytes;
+    uint32_t bad = 0;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const int64_t row = idx / row_bytes;
+        const int64_t rb = idx - row * row_bytes;
+        const int64_t g = rb / kTrit5GroupBytes;
+        const int j = int(rb - g * kTrit5GroupBytes);
+        const int8_t* src = codes + row * k + g * kGroup + 5 * j;
+        const int cnt = j < 25 ? 5 : 3;
+        uint32_t val = 0, w = 1;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const uint32_t d = i < cnt ? code_digit(src[i], bad) : 1u;
+            val += d * w;
+            w *= 3;
+        }
+        packed[idx] = uint8_t(val);
+    }
+    if (bad_count && bad) atomicAdd(bad_count, int32_t(bad));
+}
+
+// One thread per output dword of the 2-bit format (16 codes in, 4 bytes out).
+__global__ __launch_bounds__(kThreads) void pack_slot2_kernel(
+    const int8_t* __restrict__ codes, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int32_t* __restrict__ bad_count) {
+    const int64_t total = n * k / 16;
+    uint32_t bad = 0;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const int4 raw = reinterpret_cast<const int4*>(codes)[idx];
+        const int8_t* c = reinterpret_cast<const int8_t*>(&raw);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) word |= code_digit(c[i], bad) << (2 * i);
+        reinterpret_cast<uint32_t*>(packed)[idx] = word;
+    }
+    if (bad_count && bad) atomicAdd(bad_count, int32_t(bad));
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_trit5_kernel(
+    const uint8_t* __restrict__ packed, int64_t n, int64_t k, int8_t* __restrict__ codes) {
+    const int64_t row_bytes = (k / kGroup) * kTrit5GroupBytes;
+    const int64_t total = n * row_bytes;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const int64_t row = idx / row_bytes;
+        const int64_t rb = idx - row * row_bytes;
+        const int64_t g = rb / kTrit5GroupBytes;
+        const int j = int(rb - g * kTrit5GroupBytes);
+        int8_t* dst = codes + row * k + g * kGroup + 5 * j;
+        uint32_t v = packed[idx];
+        const int cnt = j < 25 ? 5 : 3;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const uint32_t q = v / 3u;
+            const uint32_t d = v - 3u * q;
+            v = q;
+            if (i < cnt) dst[i] = int8_t(int(d > 2u ? 1u : d) - 1);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void unpack_slot2_kernel(
+    const uint8_t* __restrict__ packed, int64_t n, int64_t k, int8_t* __restrict__ codes) {
+    const int64_t total = n * k / 4;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const uint32_t b = packed[idx];
+        uint32_t out = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t d = (b >> (2 * i)) & 3u;
+            d = d > 2u ? 1u : d;
+            out |= (uint32_t(uint8_t(int8_t(int(d) - 1)))) << (8 * i);
+        }
+        reinterpret_cast<uint32_t*>(codes)[idx] = out;
+    }
+}
+
+unsigned grid_for(int64_t total) {
+    int64_t blocks = (total + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    return unsigned(blocks);
+}
+
+}  // namespace
+
+hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt, uint8_t* packed,
+                       int32_t* bad_count, hipStream_t stream) {
+    if (fmt == 0) {
+        const int64_t total = n * (k / kGroup) * kTrit5GroupBytes;
+        hipLaunchKernelGGL(pack_trit5_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                           codes, n, k, packed, bad_count);
+    } else {
+        const int64_t total = n * k / 16;
+        hipLaunchKernelGGL(pack_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                           codes, n, k, packed, bad_count);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int fmt, int8_t* codes,
+                         hipStream_t stream) {
+    if (fmt == 0) {
+        const int64_t total = n * (k / kGroup) * kTrit5GroupBytes;
+        hipLaunchKernelGGL(unpack_trit5_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                           packed, n, k, codes);
+    } else {
+        const int64_t total = n * k / 4;
+        hipLaunchKernelGGL(unpack_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                           packed, n, k, codes);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tl

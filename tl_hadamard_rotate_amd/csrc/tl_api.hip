@@ -1,0 +1,141 @@
+// C ABI of libtl: argument validation, then one launch on the caller's stream.
+// Every check runs on the host before anything is enqueued, so a rejected call
+// leaves every output untouched.
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/tl.h"
+#include "tl_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr int64_t kMaxRows = int64_t(1) << 24;     // M and N
+constexpr int64_t kMaxElems = int64_t(1) << 36;    // M*K, N*K and M*N
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + uintptr_t(b_bytes) && b0 < a0 + uintptr_t(a_bytes);
+}
+
+int64_t row_bytes(int64_t k, int32_t fmt) {
+    return fmt == TL_FMT_TRIT5 ? (k / TL_GROUP) * 26 : k / 4;
+}
+
+tl_status launched(hipError_t e) {
+    if (e == hipSuccess) return TL_OK;
+    g_last_error = hipGetErrorString(e);
+    return TL_ERR_LAUNCH;
+}
+
+bool pack_shape_ok(int64_t n, int64_t k) {
+    return n >= 1 && n <= kMaxRows && k >= TL_GROUP && k % TL_GROUP == 0 && k <= TL_MAX_K &&
+           n * k <= kMaxElems;
+}
+
+bool layer_shape_ok(int64_t m, int64_t n, int64_t k) {
+    return m >= 1 && m <= kMaxRows && n >= 1 && n <= kMaxRows && k >= TL_BLOCK &&
+           k % TL_BLOCK == 0 && k <= TL_MAX_K && m * k <= kMaxElems && n * k <= kMaxElems &&
+           m * n <= kMaxElems;
+}
+
+tl_status check_layer(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                      const uint16_t* x_rot, int64_t m, int64_t n, int64_t k, void* y,
+                      int32_t y_dtype) {
+    if (!packed || !scales || !x_rot || !y) return TL_ERR_NULL;
+    if (!layer_shape_ok(m, n, k)) return TL_ERR_SHAPE;
+    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (y_dtype != TL_F32 && y_dtype != TL_F16) return TL_ERR_DTYPE;
+    if (!aligned16(packed) || !aligned16(scales) || !aligned16(x_rot) || !aligned16(y))
+        return TL_ERR_ALIGN;
+    const int64_t y_bytes = m * n * (y_dtype == TL_F32 ? 4 : 2);
+    if (overlap(y, y_bytes, packed, n * row_bytes(k, fmt)) ||
+        overlap(y, y_bytes, scales, n * (k / TL_GROUP) * 2) || overlap(y, y_bytes, x_rot, m * k * 2))
+        return TL_ERR_ALIAS;
+    return TL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tl_packed_bytes(int64_t N, int64_t K, int32_t fmt) {
+    if (N < 1 || K < TL_GROUP || K % TL_GROUP != 0) return -1;
+    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return -1;
+    return N * row_bytes(K, fmt);
+}
+
+tl_status tl_pack(const int8_t* codes, int64_t N, int64_t K, int32_t fmt, uint8_t* packed,
+                  int32_t* bad_count, hipStream_t stream) {
+    if (!codes || !packed) return TL_ERR_NULL;
+    if (!pack_shape_ok(N, K)) return TL_ERR_SHAPE;
+    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (!aligned16(codes) || !aligned16(packed)) return TL_ERR_ALIGN;
+    if (bad_count && (reinterpret_cast<uintptr_t>(bad_count) & 3u)) return TL_ERR_ALIGN;
+    const int64_t pb = N * row_bytes(K, fmt);
+    if (overlap(packed, pb, codes, N * K)) return TL_ERR_ALIAS;
+    if (bad_count && (overlap(bad_count, 4, codes, N * K) || overlap(bad_count, 4, packed, pb)))
+        return TL_ERR_ALIAS;
+    return launched(tl::launch_pack(codes, N, K, fmt, packed, bad_count, stream));
+}
+
+tl_status tl_unpack(const uint8_t* packed, int64_t N, int64_t K, int32_t fmt, int8_t* codes,
+                    hipStream_t stream) {
+    if (!codes || !packed) return TL_ERR_NULL;
+    if (!pack_shape_ok(N, K)) return TL_ERR_SHAPE;
+    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (!aligned16(codes) || !aligned16(packed)) return TL_ERR_ALIGN;
+    if (overlap(packed, N * row_bytes(K, fmt), codes, N * K)) return TL_ERR_ALIAS;
+    return launched(tl::launch_unpack(packed, N, K, fmt, codes, stream));
+}
+
+tl_status tl_hadamard_rotate(const uint16_t* x, const int8_t* signs, int64_t M, int64_t K,
+                             uint16_t* x_rot, hipStream_t stream) {
+    if (!x || !signs || !x_rot) return TL_ERR_NULL;
+    if (!(M >= 1 && M <= kMaxRows && K >= TL_BLOCK && K % TL_BLOCK == 0 && K <= TL_MAX_K &&
+          M * K <= kMaxElems))
+        return TL_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(signs) || !aligned16(x_rot)) return TL_ERR_ALIGN;
+    const int64_t bytes = M * K * 2;
+    if (x_rot != x && overlap(x_rot, bytes, x, bytes)) return TL_ERR_ALIAS;
+    if (overlap(x_rot, bytes, signs, K)) return TL_ERR_ALIAS;
+    return launched(tl::launch_hadamard(x, signs, M, K, x_rot, stream));
+}
+
+tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x_rot,
+                  int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype, hipStream_t stream) {
+    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    return launched(
+        tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
+}
+
+tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x_rot,
+                  int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype, hipStream_t stream) {
+    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    return launched(
+        tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
+}
+
+const char* tl_status_str(tl_status status) {
+    switch (status) {
+        case TL_OK: return "TL_OK";
+        case TL_ERR_NULL: return "TL_ERR_NULL";
+        case TL_ERR_SHAPE: return "TL_ERR_SHAPE";
+        case TL_ERR_FORMAT: return "TL_ERR_FORMAT";
+        case TL_ERR_ALIGN: return "TL_ERR_ALIGN";
+        case TL_ERR_ALIAS: return "TL_ERR_ALIAS";
+        case TL_ERR_LAUNCH: return "TL_ERR_LAUNCH";
+        case TL_ERR_DTYPE: return "TL_ERR_DTYPE";
+    }
+    return "TL_ERR_UNKNOWN";
+}
+
+const char* tl_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

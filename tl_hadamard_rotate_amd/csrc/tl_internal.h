@@ -1,0 +1,27 @@
+// Internal declarations shared by the HIP translation units of libtl.
+// Every launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tl {
+
+constexpr int kBlock = 1024;        // Hadamard block width
+constexpr int kGroup = 128;         // weights per binary16 scale
+constexpr int kTrit5GroupBytes = 26;
+
+hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt,
+                       uint8_t* packed, int32_t* bad_count, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int fmt,
+                         int8_t* codes, hipStream_t stream);
+hipError_t launch_hadamard(const uint16_t* x, const int8_t* signs, int64_t m, int64_t k,
+                           uint16_t* out, hipStream_t stream);
+hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt,
+                       const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                       void* y, int y_f16, hipStream_t stream);
+hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
+                       const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                       void* y, int y_f16, hipStream_t stream);
+
+}  // namespace tl
