@@ -99,13 +99,20 @@ def _rotate_gpu(x16, signs, device, inplace=False):
 
 
 @pytest.mark.parametrize("m,k", [(1, 1024), (3, 5120), (17, 2048), (64, 17408)])
-def test_rotate_random_within_one_ulp(gpu, m, k):
+def test_rotate_random_within_derived_bound(gpu, m, k):
     inp = synth.linear_inputs(1, k, m, cfg=3, linear=m, outliers=True)
     got = _rotate_gpu(inp.x, inp.signs, gpu).astype(np.float64)
     want = oracle.rotate(inp.x, inp.signs)
-    ulp = oracle.fp16_ulp(want)
-    assert np.all(np.abs(got - want) <= ulp), np.max(np.abs(got - want) / ulp)
-    # fp32 sums then one rounding: at least 99% of entries are the nearest binary16
+    # Error bound of the kernel's arithmetic: each output is a 10-level tree of
+    # fp32 additions of the 1024 terms +-x_j/32 (|error| <= 10 u sum_j |x_j|/32,
+    # u = 2^-24), followed by one rounding to binary16 (half an ulp of the
+    # larger of the two neighbouring binades).
+    xa = np.abs(inp.x.astype(np.float64)).reshape(m, k // 1024, 1024).sum(-1) / 32.0
+    fp32_err = np.repeat(10 * 2.0 ** -24 * xa, 1024, axis=1)
+    half_ulp = 0.5 * np.maximum(oracle.fp16_ulp(got), oracle.fp16_ulp(want))
+    excess = np.abs(got - want) - (half_ulp + fp32_err)
+    assert np.all(excess <= 0), np.max(excess)
+    # and nearly every entry is the correctly rounded binary16 value
     nearest = want.astype(np.float16).astype(np.float64)
     assert np.mean(got == nearest) > 0.99
 
