@@ -20,9 +20,8 @@
 // model's shapes a CU's share is only a few blocks per wave, so each wave
 // requests all the blocks it owns (up to kFlight at a time, held in
 // registers) before it waits for any of them.  The activations are copied
-// into LDS by direct global->LDS loads issued ahead of the weights; loads of a
-// wave complete in order, so waiting for them does not wait for the weights,
-// and the decode table is built while everything is in flight.  The waits are
+// into LDS by direct global->LDS loads, and the decode table is built, before
+// the weight stream starts (see the prologue).  The waits are
 // explicit counts on straight-line code (one instantiation per number of
 // blocks in flight), so no wait covers a load that is not yet needed.
 //
@@ -54,9 +53,10 @@ constexpr int kLutRows = 171;              // bytes 0..170 cover every valid cod
 constexpr int kLutBytes = kLutRows * 256;
 constexpr int kSteps = 4;                  // 64-byte chunk steps per 1024-block
 // blocks a wave keeps in flight (registers: 20 VGPRs per block)
-constexpr int flight_max(int nt) { return nt == 1 ? 3 : 2; }
-constexpr int kLoadsPerBlock = kSteps + 1; // 16-byte loads per block: codes + scales
-constexpr int kMaxWaves = 16;              // waves per workgroup
+constexpr int flight_max(int nt) { return nt == 1 ? 2 : 2; }
+// waves per workgroup: 16 (128 VGPRs each) for one pass, 8 (256 VGPRs each)
+// for two passes, whose operands need the larger register budget
+constexpr int max_waves(int nt) { return nt == 1 ? 16 : 8; }
 constexpr size_t kLdsLimit = 160 * 1024;
 
 __device__ __forceinline__ uint32_t code_bits(uint32_t d) {
@@ -81,7 +81,7 @@ __device__ __forceinline__ void load_block(Block& b, const uint8_t* wb, const ui
 // Copy 1 KB (16 bytes per lane) from global memory straight into LDS at the
 // wave-uniform byte offset lds_off.  Issued from asm so that the compiler does
 // not track it (it would otherwise wait for every load before any LDS read);
-// completion is covered by the explicit wait in wait_barrier.  No register is
+// completion is covered by the explicit wait in vm_lds_barrier.  No register is
 // written, so nothing is left in flight that the compiler could reuse.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"   // m0 is reserved, and set here on purpose
@@ -96,12 +96,11 @@ __device__ __forceinline__ void dma_1k(uint32_t lds_off, const void* src) {
 }
 #pragma clang diagnostic pop
 
-// Wait until at most N vector-memory loads of this wave are outstanding and
-// its LDS writes are done, then join the workgroup barrier.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
+// Wait for every load and LDS write of this wave (the activation copies are
+// tracked by no compiler-inserted wait), then the workgroup barrier.
+__device__ __forceinline__ void vm_lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -131,45 +130,93 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t rep, uint32_t w) {
     return __builtin_amdgcn_perm(rep, w, 0x0c0c0004u | (uint32_t(SEL_BYTE) << 8));
 }
 
-struct Lane {
-    const uint8_t* lut;
-    uint32_t rep;     // this lane's table copy * 8
-    int64_t k;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4;
+
+// Where a lane's A operand (activations) comes from.  Offsets are byte
+// offsets from the start of the wave's K range, the same for every lane.
+template <int NT, bool XLDS>
+struct XSrc;
+
+// LDS copy: per pass, the LDS byte address of the lane's activations at the
+// start of its K range, or of a 128-byte zero pad for lanes that carry none;
+// the mask keeps the pad address fixed, so no lane branches or zero-fills.
+template <int NT>
+struct XSrc<NT, true> {
+    uint32_t base[NT];
+    uint32_t mask[NT];
+    __device__ __forceinline__ uint4 get(int p, uint32_t off, int t) const {
+        return __builtin_bit_cast(
+            uint4, *reinterpret_cast<lds_u32x4*>(base[p] + (mask[p] & off) + 16u * uint32_t(t)));
+    }
 };
 
-// Decode and multiply one block into acc.  xr points at this lane's
-// activations for the block's first step (row of its A role).
+// Global memory (activations too large for LDS): lanes that carry none read
+// nothing and take zeros.
 template <int NT>
-__device__ __forceinline__ void compute_block(const Block& b, const Lane& ln, const uint16_t* xr,
-                                              const bool (&a_load)[NT], uint4 (&av)[NT],
-                                              float (&acc)[NT][2]) {
+struct XSrc<NT, false> {
+    const uint8_t* ptr[NT];
+    bool live[NT];
+    __device__ __forceinline__ uint4 get(int p, uint32_t off, int t) const {
+        return live[p] ? *reinterpret_cast<const uint4*>(ptr[p] + off + 16 * t)
+                       : uint4{0, 0, 0, 0};
+    }
+};
+
+// MFMAs per batch of operand reads: the whole step for one pass, half of it
+// for two
+template <int NT>
+constexpr int batch() { return NT == 1 ? 8 : 4; }
+
+// Decode and multiply one block into acc; off = byte offset of the block in
+// the wave's K range.  Operand reads (activation pieces and table entries) are
+// issued in batches ahead of their MFMAs, so the LDS latency is paid once per
+// batch rather than per MFMA.  The table sits at LDS address 0, so the
+// v_perm_b32 result is the entry's address.
+template <int NT, bool XLDS>
+__device__ __forceinline__ void compute_block(const Block& b, uint32_t rep, const XSrc<NT, XLDS>& xs,
+                                              uint32_t off, float (&acc)[NT][2]) {
+    constexpr int TB = batch<NT>();
 #pragma unroll
     for (int i = 0; i < kSteps; ++i) {
-        const uint32_t s2 = i == 0 ? b.s.x : (i == 1 ? b.s.y : (i == 2 ? b.s.z : b.s.w));
-        const float sc0 = __half2float(__ushort_as_half(uint16_t(s2 & 0xFFFFu)));
-        const float sc1 = __half2float(__ushort_as_half(uint16_t(s2 >> 16)));
+        const uint32_t wd[4] = {b.w[i].x, b.w[i].y, b.w[i].z, b.w[i].w};
         float4v d[NT];
 #pragma unroll
         for (int p = 0; p < NT; ++p) d[p] = float4v{0.f, 0.f, 0.f, 0.f};
-        const uint32_t wd[4] = {b.w[i].x, b.w[i].y, b.w[i].z, b.w[i].w};
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const uint32_t dw = wd[t >> 1];
-            const uint32_t a0 = (t & 1) ? lut_addr<2>(ln.rep, dw) : lut_addr<0>(ln.rep, dw);
-            const uint32_t a1 = (t & 1) ? lut_addr<3>(ln.rep, dw) : lut_addr<1>(ln.rep, dw);
-            const uint2 e0 = *reinterpret_cast<const uint2*>(ln.lut + a0);
-            const uint2 e1 = *reinterpret_cast<const uint2*>(ln.lut + a1);
-            const half8 bv = __builtin_bit_cast(half8, uint4{e0.x, e0.y, e1.x, e1.y});
+        for (int t0 = 0; t0 < 8; t0 += TB) {
+            // activations x[tok][256 s + 64 q + 8 t .. + 7] of this lane's A role
+            uint4 av[NT][TB];
 #pragma unroll
-            for (int p = 0; p < NT; ++p) {
-                // activations x[tok][256 s + 64 q + 8 t .. + 7] of this lane's A role
-                if (a_load[p])
-                    av[p] = *reinterpret_cast<const uint4*>(xr + 8 * p * ln.k + 256 * i + 8 * t);
-                d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    __builtin_bit_cast(half8, av[p]), bv, d[p], 0, 0, 0);
+            for (int p = 0; p < NT; ++p)
+#pragma unroll
+                for (int t = 0; t < TB; ++t) av[p][t] = xs.get(p, off + 512u * i, t0 + t);
+            uint2 e[2 * TB];
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const int tt = t0 + t;
+                const uint32_t dw = wd[tt >> 1];
+                const uint32_t a0 = (tt & 1) ? lut_addr<2>(rep, dw) : lut_addr<0>(rep, dw);
+                const uint32_t a1 = (tt & 1) ? lut_addr<3>(rep, dw) : lut_addr<1>(rep, dw);
+                e[2 * t] = __builtin_bit_cast(uint2, *reinterpret_cast<lds_u32x2*>(a0));
+                e[2 * t + 1] = __builtin_bit_cast(uint2, *reinterpret_cast<lds_u32x2*>(a1));
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                const half8 bv = __builtin_bit_cast(
+                    half8, uint4{e[2 * t].x, e[2 * t].y, e[2 * t + 1].x, e[2 * t + 1].y});
+#pragma unroll
+                for (int p = 0; p < NT; ++p)
+                    d[p] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(half8, av[p][t]), bv, d[p], 0, 0, 0);
             }
         }
         // D row 4q + r = token 2q + r/2 of the pass, group parity r & 1
+        const uint32_t s2 = i == 0 ? b.s.x : (i == 1 ? b.s.y : (i == 2 ? b.s.z : b.s.w));
+        const float sc0 = __half2float(__ushort_as_half(uint16_t(s2 & 0xFFFFu)));
+        const float sc1 = __half2float(__ushort_as_half(uint16_t(s2 >> 16)));
 #pragma unroll
         for (int p = 0; p < NT; ++p) {
             acc[p][0] += sc0 * d[p][0] + sc1 * d[p][1];
@@ -179,43 +226,34 @@ __device__ __forceinline__ void compute_block(const Block& b, const Lane& ln, co
 }
 
 // NR consecutive blocks of this wave's tile: all loads first, then the
-// blocks in order.  The first flight of the kernel also builds the table and
-// holds the workgroup barrier that publishes the table and the activations:
-// at that point only the NR blocks were issued after the activation copies.
-template <int NR, int NT, bool FIRST>
-__device__ __forceinline__ void flight(const uint8_t* wb, const uint16_t* sb, const uint16_t* xr,
-                                       const Lane& ln, uint8_t* lut, int tid, int nthreads,
-                                       const bool (&a_load)[NT], uint4 (&av)[NT],
+// blocks in order.
+template <int NR, int NT, bool XLDS>
+__device__ __forceinline__ void flight(const uint8_t* wb, const uint16_t* sb, uint32_t rep,
+                                       const XSrc<NT, XLDS>& xs, uint32_t off,
                                        float (&acc)[NT][2]) {
-    Block b[NR > 0 ? NR : 1];
+    Block b[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) load_block(b[i], wb + 256 * i, sb + 8 * i);
-    if (FIRST) {
-        build_lut(lut, tid, nthreads);
-        wait_barrier<kLoadsPerBlock * NR>();
-    }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) compute_block<NT>(b[i], ln, xr + 1024 * i, a_load, av, acc);
-}
-
-template <int NT, bool FIRST>
-__device__ __forceinline__ void flight_n(int nr, const uint8_t* wb, const uint16_t* sb,
-                                         const uint16_t* xr, const Lane& ln, uint8_t* lut, int tid,
-                                         int nthreads, const bool (&a_load)[NT], uint4 (&av)[NT],
-                                         float (&acc)[NT][2]) {
-    if (flight_max(NT) >= 3 && nr >= 3)
-        flight<(flight_max(NT) >= 3 ? 3 : 2), NT, FIRST>(wb, sb, xr, ln, lut, tid, nthreads,
-                                                         a_load, av, acc);
-    else if (nr >= 2)
-        flight<2, NT, FIRST>(wb, sb, xr, ln, lut, tid, nthreads, a_load, av, acc);
-    else if (nr == 1)
-        flight<1, NT, FIRST>(wb, sb, xr, ln, lut, tid, nthreads, a_load, av, acc);
-    else if (FIRST)
-        flight<0, NT, FIRST>(wb, sb, xr, ln, lut, tid, nthreads, a_load, av, acc);
+    for (int i = 0; i < NR; ++i)
+        compute_block<NT, XLDS>(b[i], rep, xs, off + 2048u * i, acc);
 }
 
 template <int NT, bool XLDS>
-__global__ __launch_bounds__(1024) void gemv_slot2_kernel(
+__device__ __forceinline__ void flight_n(int nr, const uint8_t* wb, const uint16_t* sb,
+                                         uint32_t rep, const XSrc<NT, XLDS>& xs, uint32_t off,
+                                         float (&acc)[NT][2]) {
+    constexpr int kTop = flight_max(NT) >= 3 ? 3 : 2;
+    if (kTop == 3 && nr >= 3)
+        flight<kTop, NT, XLDS>(wb, sb, rep, xs, off, acc);
+    else if (nr >= 2)
+        flight<2, NT, XLDS>(wb, sb, rep, xs, off, acc);
+    else if (nr == 1)
+        flight<1, NT, XLDS>(wb, sb, rep, xs, off, acc);
+}
+
+template <int NT, bool XLDS>
+__global__ __launch_bounds__(64 * max_waves(NT)) void gemv_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int m, int64_t n, int64_t k,
     int ksplit, void* __restrict__ y, int y_f16) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -231,20 +269,6 @@ __global__ __launch_bounds__(1024) void gemv_slot2_kernel(
     const int j = lane & 15;          // weight row in the tile (B column) / A row
     const int q = lane >> 4;          // 16-byte piece of the lane inside a chunk step
 
-    // activations -> LDS, 1 KB per wave instruction, issued before any weight
-    // load; surplus instructions repeat the last piece (same bytes, same place)
-    if (XLDS) {
-        const int pieces = int(int64_t(m) * k / 512);   // M*K is a multiple of 1024
-        const int per_wave = (pieces + nwaves - 1) / nwaves;
-        const uint32_t xs_off =
-            uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t*)(xs)));
-        for (int c = 0; c < per_wave; ++c) {
-            int idx = wave + c * nwaves;
-            idx = idx < pieces ? idx : pieces - 1;
-            dma_1k(xs_off + uint32_t(idx) * 1024u, x + int64_t(idx) * 512 + lane * 8);
-        }
-    }
-
     // this workgroup's rows, and this wave's tile and block range
     const int64_t r0 = int64_t(blockIdx.x) * n / gridDim.x;
     const int64_t r1 = int64_t(blockIdx.x + 1) * n / gridDim.x;
@@ -257,23 +281,46 @@ __global__ __launch_bounds__(1024) void gemv_slot2_kernel(
     const int64_t blocks = k / kBlock;
     const int64_t b0 = blocks * ks / ksplit;
     const int nb_tile = int(blocks * (ks + 1) / ksplit - b0);
+    const int nb = tile_slot < tiles_here ? nb_tile : 0;
 
-    const Lane ln{lut, uint32_t(lane & 31) * 8u, k};
+    // Prologue: the activations -> LDS (1 KB per wave instruction, spread over
+    // the waves) and the decode table, published by one barrier before any
+    // weight load is issued.  The activations are read by every CU; requested
+    // while the weight stream is in flight they would queue behind it in the
+    // shared memory queues and hold the first MFMA back until most weights
+    // had arrived.
+    const uint32_t xs_lds = uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t*)(xs)));
+    const uint32_t zero_lds = xs_lds + uint32_t(m) * uint32_t(k) * 2u;   // 128-byte zero pad
+    if (XLDS) {
+        const int pieces = int(int64_t(m) * k / 512);   // M*K is a multiple of 1024
+        for (int c = wave; c < pieces; c += nwaves)
+            dma_1k(xs_lds + uint32_t(c) * 1024u, x + int64_t(c) * 512 + lane * 8);
+        if (tid < 8)
+            *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(zero_lds + 16u * tid) =
+                u32x4{0, 0, 0, 0};
+    }
+    build_lut(lut, tid, nthreads);
+    vm_lds_barrier();
+
+    const uint32_t rep = uint32_t(lane & 31) * 8u;   // this lane's table copy * 8
     // A-operand role of this lane: row j of A = token j/2 of the pass, parity j&1
     const int a_tok = j >> 1, a_par = j & 1;
     const bool a_live = a_par == (q >> 1);
-    bool a_load[NT];
     float acc[NT][2];
-    uint4 av[NT];   // lanes without activations keep zeros for the whole kernel
+    XSrc<NT, XLDS> xsrc;
 #pragma unroll
     for (int p = 0; p < NT; ++p) {
         acc[p][0] = acc[p][1] = 0.0f;
-        a_load[p] = a_live && (8 * p + a_tok) < m;
-        av[p] = uint4{0, 0, 0, 0};
+        const bool live = a_live && (8 * p + a_tok) < m;
+        const int64_t xoff = int64_t(8 * p + a_tok) * k + 64 * q + kBlock * b0;   // halves
+        if constexpr (XLDS) {
+            xsrc.base[p] = live ? xs_lds + uint32_t(xoff) * 2u : zero_lds;
+            xsrc.mask[p] = live ? ~0u : 0u;
+        } else {
+            xsrc.ptr[p] = reinterpret_cast<const uint8_t*>(x + (live ? xoff : 0));
+            xsrc.live[p] = live;
+        }
     }
-    // activations of this lane's A role: LDS copy or global memory
-    const int64_t xoff = int64_t(a_tok) * k + 64 * q + kBlock * b0;
-    const uint16_t* xr = XLDS ? static_cast<const uint16_t*>(xs + xoff) : x + xoff;
 
     int64_t tile = tile_slot;
     int64_t row = r0 + 16 * tile + j;
@@ -282,15 +329,12 @@ __global__ __launch_bounds__(1024) void gemv_slot2_kernel(
     const int64_t lrow = row_ok ? row : r0;
     const uint8_t* wb = packed + lrow * row_bytes + 16 * q + 256 * b0;
     const uint16_t* sb = scales + lrow * groups + 8 * b0;
-    const int nb = tile < tiles_here ? nb_tile : 0;
 
     constexpr int kFlight = flight_max(NT);
-    int f = nb < kFlight ? nb : kFlight;
-    flight_n<NT, true>(f, wb, sb, xr, ln, lut, tid, nthreads, a_load, av, acc);
     for (;;) {   // tiles of this wave (a single one unless ksplit == 1)
-        for (; f < nb; f += kFlight)
-            flight_n<NT, false>(nb - f, wb + 256 * f, sb + 8 * f, xr + kBlock * f, ln, lut, tid,
-                                nthreads, a_load, av, acc);
+        for (int f = 0; f < nb; f += kFlight)
+            flight_n<NT, XLDS>(nb - f, wb + 256 * f, sb + 8 * f, rep, xsrc, 2048u * uint32_t(f),
+                               acc);
         tile += tile_stride;
         if (ksplit > 1 || tile >= tiles_here) break;
         // whole-K tiles: write this one out and start the next
@@ -310,7 +354,6 @@ __global__ __launch_bounds__(1024) void gemv_slot2_kernel(
         const int64_t nrow = row_ok ? row : r0;
         wb = packed + nrow * row_bytes + 16 * q;
         sb = scales + nrow * groups;
-        f = 0;
     }
 
 #pragma unroll
@@ -354,18 +397,18 @@ struct Plan {
 };
 
 // one workgroup per CU, each with an equal share of the rows; the waves of a
-// workgroup split K when the share is at most 16 tiles
-Plan make_plan(int64_t n) {
+// workgroup split K when the share is at most max_waves tiles
+Plan make_plan(int64_t n, int max_w) {
     Plan p;
     const int64_t tiles = (n + 15) / 16;
     p.grid = tiles < num_cus() ? tiles : num_cus();
     const int64_t rows_per_wg = (n + p.grid - 1) / p.grid;
     const int64_t tiles_per_wg = (rows_per_wg + 15) / 16;
-    if (tiles_per_wg >= kMaxWaves) {
+    if (tiles_per_wg >= max_w) {
         p.ksplit = 1;
-        p.waves = kMaxWaves;
+        p.waves = max_w;
     } else {
-        p.ksplit = int(kMaxWaves / tiles_per_wg);
+        p.ksplit = int(max_w / tiles_per_wg);
         p.waves = int(tiles_per_wg) * p.ksplit;
     }
     return p;
@@ -384,7 +427,7 @@ hipError_t launch_one(const Plan& plan, const uint8_t* packed, const uint16_t* s
         attr_set = true;
     }
     size_t lds = size_t(kLutBytes) + size_t(plan.waves) * NT * 2 * 64 * 4 +
-                 (XLDS ? size_t(mt) * size_t(k) * 2 : 0);
+                 (XLDS ? size_t(mt) * size_t(k) * 2 + 128 : 0);
     // ask for more than half of the CU's LDS so that two workgroups never share a CU
     if (lds < kLdsLimit / 2 + 1024) lds = kLdsLimit / 2 + 1024;
     hipLaunchKernelGGL((gemv_slot2_kernel<NT, XLDS>), dim3(unsigned(plan.grid)),
@@ -399,16 +442,20 @@ hipError_t launch_gemv_slot2(const uint8_t* packed, const uint16_t* scales, cons
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream) {
     const int64_t y_elem = y_f16 ? 2 : 4;
-    const Plan plan = make_plan(n);
-    // activations go to LDS when they fit beside the table and the reduction buffer
-    const int64_t x_lds_budget = int64_t(kLdsLimit) - kLutBytes - kMaxWaves * 2 * 2 * 64 * 4;
+    // up to 16 tokens per launch: one pass of 8, or two passes sharing the decode
     for (int64_t m0 = 0; m0 < m; m0 += 16) {
         const int mt = int(m - m0 < 16 ? m - m0 : 16);
+        const int nt = mt <= 8 ? 1 : 2;
+        const Plan plan = make_plan(n, max_waves(nt));
         const uint16_t* xs = x + m0 * k;
         void* ys = static_cast<uint8_t*>(y) + m0 * n * y_elem;
-        const bool fits = int64_t(mt) * k * 2 <= x_lds_budget;
+        // activations go to LDS (with a 128-byte zero pad) when they fit beside
+        // the table and the reduction buffer
+        const int64_t x_lds_budget =
+            int64_t(kLdsLimit) - kLutBytes - int64_t(plan.waves) * nt * 2 * 64 * 4;
+        const bool fits = int64_t(mt) * k * 2 + 128 <= x_lds_budget;
         hipError_t e;
-        if (mt <= 8)
+        if (nt == 1)
             e = fits ? launch_one<1, true>(plan, packed, scales, xs, mt, n, k, ys, y_f16, stream)
                      : launch_one<1, false>(plan, packed, scales, xs, mt, n, k, ys, y_f16, stream);
         else
