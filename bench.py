@@ -3,32 +3,45 @@
 A step is one decode pass (M = 1) over the 27B-class MLP projections
 gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120): for
 each projection the signed 1024-block Hadamard rotation of its input followed
-by the ternary GEMV.  Inputs are seeded synthetic tensors with the workload's
-distributions.  The weights are replicated into --copies distinct device
-buffers and the steps cycle through them, so that no step finds its weights in
-the 256 MB last-level cache.
+by the ternary GEMV (6 kernels).  Inputs are seeded synthetic tensors with the
+workload's distributions.
+
+Timing.  Each step is captured once in a HIP graph; the weights are replicated
+into --copies distinct buffers (one graph per copy) and the timed loop cycles
+through them, so no step finds its weights in the 256 MB last-level cache.
+W warm-up steps, then exactly K timed steps between two HIP events on the
+launch stream, with a device synchronisation on both sides.
+
+The dominant kernel (the GEMV) is also timed on its own: a graph of the three
+GEMV launches per weight copy, replayed between HIP events on the same
+stream; the average launch duration gives the roofline figure.  HBM traffic of
+the GEMV comes from the rocprofv3 counter summary under profiles/, and is
+reported only while the kernel source is the one those counters were taken
+from.
 
 Prints one JSON line on stdout; progress goes to stderr.
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
-
-import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "ternary GEMV GB/s (% HBM peak) + prefill GEMM TFLOP/s at 27B-class shapes"
-HBM_PEAK_GBS = 8000.0
-MFMA_F16_PEAK_TFLOPS = 2516.6
+HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 STEP_LINEARS = ("gate", "up", "down")
+FMT_NAMES = {"trit5": 0, "slot2": 1}
+KERNEL_SRC = {0: "gemv.hip", 1: "gemv_slot2.hip"}
 
 
 def log(msg: str) -> None:
@@ -47,8 +60,29 @@ def rotate_bytes(m: int, k: int) -> int:
     return 2 * m * k * 2 + k
 
 
+def source_sha(fmt: int) -> str:
+    path = os.path.join(ROOT, "tl_hadamard_rotate_amd", "csrc", KERNEL_SRC[fmt])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(fmt: int):
+    """HBM bytes per GEMV launch from the committed counter summary, or None
+    when there is none for the current kernel source."""
+    name = "gemv_slot2" if fmt == 1 else "gemv_trit5"
+    path = os.path.join(ROOT, "profiles", f"{name}_decode_mlp_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != source_sha(fmt):
+        return None
+    return float(val.group(1))
+
+
 def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
-    per_linear = []
+    lins = []
     for name in STEP_LINEARS:
         k, n = synth.SHAPES[name]
         inp = synth.linear_inputs(n, k, 1, seed=0, cfg=2, layer=0, linear=synth.LINEAR_ID[name])
@@ -58,180 +92,93 @@ def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
         scales = torch.from_numpy(inp.scales).to(dev)
         packs = [packed] + [packed.clone() for _ in range(copies - 1)]
         scs = [scales] + [scales.clone() for _ in range(copies - 1)]
-        per_linear.append(dict(
+        lins.append(dict(
             name=name, n=n, k=k, packs=packs, scales=scs,
             x=torch.from_numpy(inp.x).to(dev), signs=torch.from_numpy(inp.signs).to(dev),
             x_rot=torch.empty((1, k), dtype=torch.float16, device=dev),
-            y=torch.empty((1, n), dtype=torch.float32, device=dev), inp=inp))
-    return per_linear
+            y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    return lins
 
 
-def run_steps(torch, tl, lins, fmt, steps, warmup, copies, time_kernels=True):
-    def step(i, evs=None):
-        c = i % copies
-        for lin in lins:
-            tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
-            if evs is not None:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record()
-                tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
-                b.record()
-                evs.append((lin["name"], a, b))
-            else:
-                tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
+def step_fn(tl, lins, fmt, c):
+    for lin in lins:
+        tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
+        tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
 
-    for i in range(warmup):
-        step(i)
+
+def gemv_fn(tl, lins, fmt, c):
+    for lin in lins:
+        tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
+
+
+def capture(torch, fn, copies, stream):
+    graphs = []
+    for c in range(copies):
+        fn(c)                                  # eager first call: one-time set-up
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn(c)
+        graphs.append(g)
     torch.cuda.synchronize()
-    evs = [] if time_kernels else None
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(steps):
-        step(warmup + i, evs)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / steps
-    kern = {}
-    if evs:
-        for name, a, b in evs:
-            kern.setdefault(name, []).append(a.elapsed_time(b))
-    return ms, wall, kern
+    return graphs
 
 
-def step_bytes(lins, fmt):
-    return sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
+def timed_replays(torch, graphs, count, warmup, stream):
+    """Replay graphs[i % len] for i in [0, count) between two HIP events on
+    `stream`; returns the elapsed milliseconds."""
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(count):
+            graphs[(warmup + i) % len(graphs)].replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+    return start.elapsed_time(end)
 
 
-def cpu_baseline(oracle, lins, fmt, tl, budget_s=12.0):
+def cpu_baseline(oracle, synth, fmt, budget_s=12.0, rows=512):
     """The oracle as it stands, timed on the host on a bounded sample: the
-    rotation plus unpack/dequant/fp64 matmul of the first rows of each
-    projection.  Reported in the metric's unit (algorithmic GB/s)."""
+    rotation plus unpack, dequantisation and fp64 matrix-vector product of the
+    first `rows` rows of gate, up and down.  Reported in GB/s of the same
+    algorithmic bytes as the GPU figure."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    rows = 512
     samples = []
-    for lin in lins:
-        inp = lin["inp"]
-        packed = oracle.pack(inp.codes[:rows], fmt)
-        samples.append((inp, packed, lin["k"]))
-    done_bytes, t0, reps = 0, time.perf_counter(), 0
+    for name in STEP_LINEARS:
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(rows, k, 1, seed=0, cfg=2, layer=0, linear=synth.LINEAR_ID[name])
+        samples.append((inp, oracle.pack(inp.codes, fmt), k))
+    done, t0, passes = 0, time.perf_counter(), 0
     while True:
         for inp, packed, k in samples:
             x_rot = oracle.rotate(inp.x, inp.signs)
-            oracle.matvec_packed(packed, inp.scales[:rows], fmt, x_rot, k)
-            done_bytes += gemv_bytes(rows, k, 1, fmt) + rotate_bytes(1, k)
-        reps += 1
+            oracle.matvec_packed(packed, inp.scales, fmt, x_rot, k)
+            done += gemv_bytes(rows, k, 1, fmt) + rotate_bytes(1, k)
+        passes += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {rows} rows of gate, up and down at M=1 (rotate + unpack + "
-                      f"fp64 dequant matmul), {reps} passes in {dt:.1f} s"}
+            "sample": f"first {rows} rows of gate, up and down at M=1 (rotation + unpack + "
+                      f"fp64 dequantised matrix-vector product), {passes} passes in {dt:.1f} s"}
 
 
-def main(argv=None) -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--fmt", choices=("trit5", "slot2"), default="trit5")
-    ap.add_argument("--copies", type=int, default=16,
-                    help="distinct weight copies cycled through (defeats the last-level cache)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extra", action="store_true", help="skip the SLOT2 and GEMM side figures")
-    args = ap.parse_args(argv)
-
-    if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(--gpus must be 1)", file=sys.stderr)
-        return 2
-
-    import torch
-
-    import synth
-    import tl_hadamard_rotate_amd as tl
-
-    dev = torch.device("cuda:0")
-    fmt = tl.FMT_TRIT5 if args.fmt == "trit5" else tl.FMT_SLOT2
-    log(f"building inputs fmt={args.fmt} copies={args.copies}")
-    lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
-    log("timing")
-    ms, wall, kern = run_steps(torch, tl, lins, fmt, args.steps, args.warmup, args.copies)
-    sbytes = step_bytes(lins, fmt)
-    value = sbytes / (ms * 1e-3) / 1e9
-
-    # dominant kernel: the GEMV; algorithmic bytes over its average launch time
-    g_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) * args.steps
-    g_ms = sum(sum(v) for v in kern.values())
-    g_launches = sum(len(v) for v in kern.values())
-    achieved = g_bytes / (g_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "tl_gemv", "launches": g_launches,
-                "avg_launch_us": round(g_ms * 1e3 / max(g_launches, 1), 3),
-                "per_linear_us": {k: round(1e3 * float(np.mean(v)), 3) for k, v in kern.items()}}
-    log(f"step {ms:.4f} ms, {value:.1f} GB/s; gemv {achieved:.1f} GB/s")
-
-    extra = {}
-    if not args.no_extra:
-        other = tl.FMT_SLOT2 if fmt == tl.FMT_TRIT5 else tl.FMT_TRIT5
-        del lins
-        torch.cuda.empty_cache()
-        lins2 = build_step_inputs(torch, tl, synth, dev, other, args.copies)
-        ms2, _, kern2 = run_steps(torch, tl, lins2, other, args.steps, args.warmup, args.copies)
-        g2 = sum(gemv_bytes(l["n"], l["k"], 1, other) for l in lins2) * args.steps
-        extra["other_format"] = {
-            "fmt": "slot2" if other == tl.FMT_SLOT2 else "trit5",
-            "step_GBs": round(step_bytes(lins2, other) / (ms2 * 1e-3) / 1e9, 1),
-            "ms_per_step": round(ms2, 5),
-            "gemv_GBs": round(g2 / (sum(sum(v) for v in kern2.values()) * 1e-3) / 1e9, 1)}
-        del lins2
-        torch.cuda.empty_cache()
-        extra["gemm"] = bench_gemm(torch, tl, synth, dev, fmt)
-        lins = None
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        log("timing the CPU oracle sample")
-        lins_cpu = [dict(n=synth.SHAPES[n][1], k=synth.SHAPES[n][0],
-                         inp=synth.linear_inputs(512, synth.SHAPES[n][0], 1, seed=0, cfg=2,
-                                                 layer=0, linear=synth.LINEAR_ID[n]))
-                    for n in STEP_LINEARS]
-        cpu = cpu_baseline(oracle, lins_cpu, fmt, tl)
-
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "decode step M=1 over 27B-class MLP projections gate/up "
-                               "(K=5120, N=17408) and down (K=17408, N=5120): signed "
-                               "1024-block Hadamard rotation + ternary g128 GEMV per "
-                               "projection; fp16 activations, fp32 accumulation",
-                   "format": args.fmt, "M": 1, "weight_copies": args.copies,
-                   "step_bytes": sbytes},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "extra": extra,
-    }
-    print(json.dumps(out), flush=True)
-    return 0
-
-
-def bench_gemm(torch, tl, synth, dev, fmt, m=2048, reps=5):
+def bench_gemm(torch, tl, synth, dev, fmt, m=2048, reps=10):
     """Prefill GEMM TFLOP/s at M=2048, K=5120, N=17408 (side figure)."""
     k, n = synth.SHAPES["gate"]
     inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=4)
     packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
     scales = torch.from_numpy(inp.scales).to(dev)
-    x = torch.randn((m, k), device=dev, dtype=torch.float32).to(torch.float16)
+    gen = torch.Generator(device="cpu").manual_seed(4)
+    x = torch.randn((m, k), generator=gen).to(torch.float16).to(dev)
     y = torch.empty((m, n), dtype=torch.float32, device=dev)
     tl.gemm(packed, scales, fmt, x, out=y)
     torch.cuda.synchronize()
@@ -245,6 +192,133 @@ def bench_gemm(torch, tl, synth, dev, fmt, m=2048, reps=5):
     tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
     return {"M": m, "K": k, "N": n, "ms": round(ms, 4), "TFLOPs": round(tflops, 2),
             "frac_of_fp16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
+def profile_pass(torch, tl, synth, dev, fmt) -> int:
+    """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
+    256 MiB written per launch) and the step's GEMVs (10 launches per shape,
+    weights cycled over 8 copies)."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    lins = build_step_inputs(torch, tl, synth, dev, fmt, 8)
+    for lin in lins:
+        tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
+    for i in range(10):
+        gemv_fn(tl, lins, fmt, i % 8)
+    torch.cuda.synchronize()
+    log("profile pass done")
+    return 0
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--fmt", choices=tuple(FMT_NAMES), default="slot2")
+    ap.add_argument("--copies", type=int, default=8,
+                    help="distinct weight copies cycled through (defeats the last-level cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other-format and GEMM figures")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="for counter runs under rocprofv3: a 256 MiB device copy (the calibration "
+                         "kernel, 3 launches) then 10 eager passes of the step's GEMVs; no timing")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    import tl_hadamard_rotate_amd as tl
+
+    dev = torch.device("cuda:0")
+    fmt = FMT_NAMES[args.fmt]
+    stream = torch.cuda.Stream(dev)
+    if args.profile_pass:
+        return profile_pass(torch, tl, synth, dev, fmt)
+    log(f"building inputs fmt={args.fmt} copies={args.copies}")
+    lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
+    with torch.cuda.stream(stream):
+        step_graphs = capture(torch, lambda c: step_fn(tl, lins, fmt, c), args.copies, stream)
+        gemv_graphs = capture(torch, lambda c: gemv_fn(tl, lins, fmt, c), args.copies, stream)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms = timed_replays(torch, step_graphs, args.steps, args.warmup, stream) / args.steps
+    sbytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
+    value = sbytes / (ms * 1e-3) / 1e9
+
+    # dominant kernel: the GEMV, timed alone (3 launches per replay)
+    reps = max(args.steps, 3 * args.copies)
+    g_ms = timed_replays(torch, gemv_graphs, reps, args.warmup, stream)
+    launches = 3 * reps
+    avg_us = g_ms * 1e3 / launches
+    per_launch = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+    achieved = per_launch / (avg_us * 1e-6) / 1e9
+    traffic = traffic_from_profiles(fmt)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None if traffic is None else round(traffic),
+                "kernel": "tl_gemv (" + ("gemv_slot2_kernel" if fmt == 1 else "gemv_simple_kernel")
+                          + ")",
+                "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": round(per_launch)}
+    log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; gemv avg {avg_us:.2f} us/launch, "
+        f"{achieved:.1f} GB/s")
+    del step_graphs, gemv_graphs
+
+    extra = {}
+    if not args.no_extra:
+        other = 1 - fmt
+        del lins
+        torch.cuda.empty_cache()
+        lins2 = build_step_inputs(torch, tl, synth, dev, other, args.copies)
+        with torch.cuda.stream(stream):
+            sg = capture(torch, lambda c: step_fn(tl, lins2, other, c), args.copies, stream)
+            gg = capture(torch, lambda c: gemv_fn(tl, lins2, other, c), args.copies, stream)
+        ms2 = timed_replays(torch, sg, args.steps, args.warmup, stream) / args.steps
+        g2 = timed_replays(torch, gg, reps, args.warmup, stream)
+        b2 = sum(gemv_bytes(l["n"], l["k"], 1, other) for l in lins2) / 3.0
+        extra["other_format"] = {
+            "fmt": "slot2" if other == 1 else "trit5",
+            "step_GBs": round(sum(gemv_bytes(l["n"], l["k"], 1, other) + rotate_bytes(1, l["k"])
+                                  for l in lins2) / (ms2 * 1e-3) / 1e9, 1),
+            "ms_per_step": round(ms2, 5),
+            "gemv_avg_launch_us": round(g2 * 1e3 / (3 * reps), 3),
+            "gemv_GBs": round(b2 / (g2 * 1e-3 / (3 * reps)) / 1e9, 1)}
+        del sg, gg, lins2
+        torch.cuda.empty_cache()
+        log("prefill GEMM side figure")
+        extra["gemm_prefill"] = bench_gemm(torch, tl, synth, dev, fmt)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle   # the checker, timed as the CPU baseline; the GPU path never uses it
+        log("timing the CPU oracle sample")
+        cpu = cpu_baseline(oracle, synth, fmt)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "decode step M=1 over 27B-class MLP projections gate/up "
+                               "(K=5120, N=17408) and down (K=17408, N=5120): signed "
+                               "1024-block Hadamard rotation + ternary g128 GEMV per "
+                               "projection; binary16 activations, fp32 accumulation",
+                   "format": args.fmt, "M": 1, "weight_copies": args.copies,
+                   "step_bytes": sbytes},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
 
 
 if __name__ == "__main__":
