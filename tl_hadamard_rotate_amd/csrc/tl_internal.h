@@ -23,6 +23,9 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt,
 hipError_t launch_gemv_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
+hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                             int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                             hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, hipStream_t stream);
