@@ -1,13 +1,26 @@
 // Prefill ternary g128 GEMM: y[m, n] = sum_k x[m, k] * code[n, k] * S[n, k/128].
-// The weight tile of each K step (one 128-group) is expanded on chip to exact
-// binary16 values code * S (a code in {-1,0,1} times a binary16 scale is a
-// binary16 number) and the contraction runs on fp16 matrix cores with fp32
-// accumulation.  Prompt processing is the practical bottleneck the pages name
-// for slower chips (page "A 27-billion model that fits in 8.6 GB", paragraph 4).
+// Weight tiles are dequantised on chip to exact binary16 values code * S (a
+// code in {-1, 0, 1} times a binary16 scale is a binary16 number) and the
+// contraction runs on the fp16 matrix cores (v_mfma_f32_16x16x32_f16) with
+// fp32 accumulation; this is the one dense contraction of the layer.  Prompt
+// processing is the bottleneck the pages name for slower chips (page "A
+// 27-billion model that fits in 8.6 GB", paragraph 4).
 //
-// Baseline tiling: 64 x 64 output tile per workgroup of 4 waves, each wave a
-// 32 x 32 quadrant made of 2 x 2 v_mfma_f32_16x16x32_f16.  A and B tiles are
-// stored K-contiguous in LDS with an 8-half row pad.
+// Tiling: a workgroup of 8 waves computes a 128 x 256 output tile (M x N);
+// wave w owns the 64 x 64 sub-tile (w / 4, w % 4), 4 x 4 MFMA tiles.  K runs in
+// steps of BK = 64 through two LDS stages:
+//   - activations: copied global -> LDS by direct loads (1 KB per wave
+//     instruction), no registers involved;
+//   - weights: the packed bytes of the next step are loaded into registers,
+//     decoded through a small LDS table, multiplied by their scale (packed
+//     fp16) and written to the other stage while the current step's MFMAs run;
+//   - one barrier per K step.
+// Both tiles are stored [row][64 halves] with the 16-byte chunks of row r
+// permuted by c -> c ^ ((r >> 1) & 7), so that the 16 lanes a 128-bit LDS read
+// serves per cycle (16 rows, one chunk) hit 16 distinct bank groups.
+// Workgroups are mapped so that each XCD (blockIdx % 8) runs a contiguous run
+// of tiles, N fastest: concurrent workgroups of an XCD share activation rows
+// in that XCD's L2.
 #include <hip/hip_fp16.h>
 
 #include "tl_internal.h"
@@ -17,141 +30,345 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
-constexpr int kThreads = 256;
-constexpr int BM = 64, BN = 64, BK = kGroup;
-constexpr int kLdsStride = BK + 8;   // halves per LDS row
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kAStage = BM * BK * 2;          // 16 KB
+constexpr int kBStage = BN * BK * 2;          // 32 KB
+constexpr int kStage = kAStage + kBStage;
+constexpr int kCopies = 8;                    // decode-table copies (bank spread)
+// decode table: TRIT5 entry = five codes in 16 bytes, SLOT2 entry = four codes
+// in 8 bytes; copy c of entry v at v * (kCopies * entry) + c * entry
+template <int FMT>
+constexpr int entry_bytes() { return FMT == 0 ? 16 : 8; }
+template <int FMT>
+constexpr int lut_bytes() { return 256 * kCopies * entry_bytes<FMT>(); }
+template <int FMT>
+constexpr int lds_bytes() { return lut_bytes<FMT>() + 2 * kStage; }
 
-// digit d -> binary16 bits of (d - 1) * s, with s given as binary16 bits
-__device__ __forceinline__ uint16_t code_times_scale(uint32_t d, uint16_t s) {
-    return d == 1u ? uint16_t(0) : (d == 0u ? uint16_t(s ^ 0x8000u) : s);
+// byte offset of 16-byte chunk c of row r in a [rows][64 halves] tile
+__device__ __forceinline__ uint32_t swz(int r, int c) {
+    return uint32_t(r) * 128u + 16u * uint32_t(c ^ ((r >> 1) & 7));
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// Copy 1 KB (16 bytes per lane) from global memory straight into LDS at the
+// wave-uniform byte offset lds_off.  Issued from asm so that the compiler does
+// not track it; completion is covered by the wait in vm_lds_barrier.  No
+// register is written.
+__device__ __forceinline__ void dma_1k(uint32_t lds_off, const void* src) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(lds_off), "v"(src)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ void vm_lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ uint32_t code_bits(uint32_t d) {
+    // digit -> binary16 bits of (d - 1); an invalid digit decodes to 0
+    return d == 0u ? 0xBC00u : (d == 2u ? 0x3C00u : 0u);
 }
 
 template <int FMT>
-__global__ __launch_bounds__(kThreads) void gemm_simple_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-    const uint16_t* __restrict__ x, int64_t m, int64_t n, int64_t k, void* __restrict__ y,
-    int y_f16) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLdsStride];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * kLdsStride];
+__device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
+    for (int c = tid; c < lut_bytes<FMT>() / 16; c += kThreads) {
+        if (FMT == 0) {
+            const uint32_t v = uint32_t(c) / kCopies;       // one 16-byte entry per piece
+            uint32_t h[5] = {0, 0, 0, 0, 0};
+            if (v < 243) {
+                uint32_t r = v;
+#pragma unroll
+                for (int i = 0; i < 5; ++i) {
+                    h[i] = code_bits(r % 3u);
+                    r /= 3u;
+                }
+            }
+            reinterpret_cast<uint4*>(lut)[c] =
+                uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
+        } else {
+            const uint32_t v = uint32_t(c) / (kCopies / 2);   // two 8-byte copies per piece
+            const uint32_t lo = code_bits(v & 3u) | (code_bits((v >> 2) & 3u) << 16);
+            const uint32_t hi = code_bits((v >> 4) & 3u) | (code_bits((v >> 6) & 3u) << 16);
+            reinterpret_cast<uint4*>(lut)[c] = uint4{lo, hi, lo, hi};
+        }
+    }
+}
+
+// binary16 pair times the scale pair (exact: codes are -1, 0, 1)
+__device__ __forceinline__ uint32_t scale_pair(uint32_t codes, half2v s2) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, codes) * s2);
+}
+
+// Packed bytes of one K step for this thread's weight row and half (32 codes).
+struct BRaw {
+    uint32_t d[7];    // TRIT5: the group's 26 bytes from byte (26g & 3); SLOT2: d[0..1]
+    uint16_t s;       // the row's scale for this step's group
+};
+
+template <int FMT>
+__device__ __forceinline__ void load_b(BRaw& r, const uint8_t* prow, const uint16_t* srow, int t) {
+    const int g = t >> 1;
+    if (FMT == 0) {
+        // 28 bytes from the dword holding the group's first byte: in bounds
+        // for every group (the last group of a row starts at 2 mod 4)
+        const uint8_t* a = prow + 26 * g - ((26 * g) & 3);
+        const uint4 lo = *reinterpret_cast<const uint4*>(a);
+        const uint4 hi = *reinterpret_cast<const uint4*>(a + 12);
+        r.d[0] = lo.x; r.d[1] = lo.y; r.d[2] = lo.z; r.d[3] = lo.w;
+        r.d[4] = hi.y; r.d[5] = hi.z; r.d[6] = hi.w;
+    } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(prow + 16 * t);
+        r.d[0] = v.x;
+        r.d[1] = v.y;
+    }
+    r.s = srow[g];
+}
+
+// LDS address of the table entry for the byte at bit position `shift` of
+// word w, in this lane's copy (rep = table base + copy offset)
+template <int FMT>
+__device__ __forceinline__ uint32_t lut_off(uint32_t w, int shift, uint32_t rep) {
+    return __builtin_amdgcn_ubfe(w, shift, 8) * uint32_t(kCopies * entry_bytes<FMT>()) + rep;
+}
+
+// TRIT5: codes (c, c + 1) of a group from the entries of the byte holding c
+// and of the next byte
+__device__ __forceinline__ uint32_t code_pair(int digit, const uint4& e, const uint4& en) {
+    switch (digit) {
+        case 0: return e.x;
+        case 1: return __builtin_amdgcn_perm(e.y, e.x, 0x05040302u);   // e.x hi, e.y lo
+        case 2: return e.y;
+        case 3: return __builtin_amdgcn_perm(e.z, e.y, 0x05040302u);   // e.y hi, e.z lo
+        default: return __builtin_amdgcn_perm(en.x, e.z, 0x05040100u); // e.z lo, en.x lo
+    }
+}
+
+// Decode 32 codes (TRIT5 codes [cs, cs + 32) of the group; the group's byte i
+// sits at byte i + o of r.d) into 16 scaled binary16 pairs.
+template <int CS, int O>
+__device__ __forceinline__ void decode_t5(const BRaw& r, uint32_t rep, half2v s2, uint32_t (&out)[16]) {
+    constexpr int b_lo = CS / 5, b_hi = (CS + 31) / 5;
+    uint4 e[b_hi - b_lo + 1];
+#pragma unroll
+    for (int b = b_lo; b <= b_hi; ++b) {
+        const int p = b + O;
+        e[b - b_lo] = __builtin_bit_cast(
+            uint4, *reinterpret_cast<lds_u32x4*>(lut_off<0>(r.d[p >> 2], 8 * (p & 3), rep)));
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = CS + 2 * i;
+        const int b = c / 5 - b_lo;
+        out[i] = scale_pair(code_pair(c % 5, e[b], e[b + (c % 5 == 4 ? 1 : 0)]), s2);
+    }
+}
+
+template <int FMT>
+__device__ __forceinline__ void decode_b(const BRaw& r, int t, int hh, uint32_t rep,
+                                         uint32_t (&out)[16]) {
+    const half2v s2 = half2v{__builtin_bit_cast(_Float16, r.s), __builtin_bit_cast(_Float16, r.s)};
+    if (FMT == 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint2 e = __builtin_bit_cast(
+                uint2, *reinterpret_cast<lds_u32x2*>(lut_off<1>(r.d[i >> 2], 8 * (i & 3), rep)));
+            out[2 * i] = scale_pair(e.x, s2);
+            out[2 * i + 1] = scale_pair(e.y, s2);
+        }
+    } else {
+        // wave-uniform: which 32 codes of the group, and the group's byte offset
+        const int cs = 64 * (t & 1) + 32 * hh;
+        const int o = (26 * (t >> 1)) & 3;
+        switch (cs + o) {
+            case 0: decode_t5<0, 0>(r, rep, s2, out); break;
+            case 2: decode_t5<0, 2>(r, rep, s2, out); break;
+            case 32: decode_t5<32, 0>(r, rep, s2, out); break;
+            case 34: decode_t5<32, 2>(r, rep, s2, out); break;
+            case 64: decode_t5<64, 0>(r, rep, s2, out); break;
+            case 66: decode_t5<64, 2>(r, rep, s2, out); break;
+            case 96: decode_t5<96, 0>(r, rep, s2, out); break;
+            default: decode_t5<96, 2>(r, rep, s2, out); break;
+        }
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(
+    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m, int64_t n,
+    int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int chunk) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const uint32_t lds0 = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(smem)));
+    const uint32_t st0 = lds0 + lut_bytes<FMT>();       // stage s at st0 + s * kStage
+
+    // XCD-aware tile order: XCD (blockIdx % 8) takes tiles [xcd * chunk, ...)
+    const int tile = int(blockIdx.x & 7) * chunk + int(blockIdx.x >> 3);
+    if (tile >= tiles) return;
+    const int64_t m0 = int64_t(tile / tiles_n) * BM;
+    const int64_t n0 = int64_t(tile % tiles_n) * BN;
+
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int64_t n_tiles = (n + BN - 1) / BN;
-    const int64_t m_base = (int64_t(blockIdx.x) / n_tiles) * BM;
-    const int64_t n_base = (int64_t(blockIdx.x) % n_tiles) * BN;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int ksteps = int(k / BK);
     const int64_t groups = k / kGroup;
     const int64_t row_bytes = FMT == 0 ? groups * kTrit5GroupBytes : k / 4;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
 
-    float4v acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+    // weight row and half of this thread for the decode: one row per lane,
+    // waves 0-3 the first 32 codes of a step, waves 4-7 the last 32
+    const int b_row = (wave & 3) * 64 + lane;
+    const int hh = wave >> 2;
+    const int64_t gn = n0 + b_row < n ? n0 + b_row : n - 1;   // rows past N decode row N-1
+    const uint8_t* prow = packed + gn * row_bytes + (FMT == 1 ? 8 * hh : 0);
+    const uint16_t* srow = scales + gn * groups;
+    const uint32_t rep = lds0 + uint32_t(lane & (kCopies - 1)) * uint32_t(entry_bytes<FMT>());
 
-    for (int64_t g = 0; g < groups; ++g) {
-        // A tile: 64 rows x 128 halves; thread -> (row, 32-half chunk)
-        {
-            const int r = tid >> 2, c = (tid & 3) * 32;
-            const int64_t gm = m_base + r;
-            uint4 v[4];
-            if (gm < m) {
-                const uint4* src = reinterpret_cast<const uint4*>(x + gm * k + g * kGroup + c);
+    // activation rows of this thread's DMA lanes: wave w copies 1 KB pieces w
+    // and w + 8 of the 16 KB A stage; piece i = rows 8i..8i+7, lane l -> row
+    // 8i + l/8, physical chunk l % 8 holding logical chunk (l%8) ^ ((row>>1)&7)
+    const uint16_t* a_src[2];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = src[i];
-            } else {
+    for (int h = 0; h < 2; ++h) {
+        const int r = 8 * (wave + 8 * h) + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int64_t gm = m0 + r < m ? m0 + r : m - 1;        // rows past M copy row M-1
+        a_src[h] = x + gm * k + 8 * c;
+    }
+
+    build_lut<FMT>(smem, tid);
+
+    auto issue_a = [&](int t, int s) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = uint4{0, 0, 0, 0};
-            }
-            uint4* dst = reinterpret_cast<uint4*>(As + r * kLdsStride + c);
+        for (int h = 0; h < 2; ++h)
+            dma_1k(st0 + uint32_t(s) * kStage + 1024u * uint32_t(wave + 8 * h), a_src[h] + BK * t);
+    };
+    auto store_b = [&](const uint32_t (&v)[16], int s) {
+        const uint32_t base = st0 + uint32_t(s) * kStage + kAStage;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = v[i];
+        for (int c = 0; c < 4; ++c)
+            *reinterpret_cast<lds_u32x4*>(base + swz(b_row, 4 * hh + c)) =
+                u32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
+    };
+
+    // prologue: step 0 into stage 0
+    BRaw braw;
+    issue_a(0, 0);
+    load_b<FMT>(braw, prow, srow, 0);
+    lds_barrier();   // the decode table
+    {
+        uint32_t v[16];
+        decode_b<FMT>(braw, 0, hh, rep, v);
+        store_b(v, 0);
+    }
+    vm_lds_barrier();
+
+    const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
+    float4v acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+
+    for (int t = 0; t < ksteps; ++t) {
+        const int s = t & 1;
+        const bool more = t + 1 < ksteps;
+        if (more) {
+            issue_a(t + 1, s ^ 1);
+            load_b<FMT>(braw, prow, srow, t + 1);
         }
-        // B tile: 64 weight rows x 128 codes, expanded to code * scale
-        {
-            const int r = tid >> 2, part = tid & 3;
-            const int64_t gn = n_base + r;
-            uint16_t* dst = Bs + r * kLdsStride;
-            if (gn < n) {
-                const uint16_t s = scales[gn * groups + g];
-                if (FMT == 0) {
-                    const uint8_t* p = packed + gn * row_bytes + g * kTrit5GroupBytes;
-                    const int j0 = part < 2 ? part * 7 : 14 + (part - 2) * 6;
-                    const int j1 = part < 2 ? j0 + 7 : j0 + 6;
-                    for (int j = j0; j < j1; ++j) {
-                        uint32_t v = p[j];
-                        const int cnt = j < 25 ? 5 : 3;
-                        for (int i = 0; i < cnt; ++i) {
-                            const uint32_t qd = v / 3u;
-                            dst[5 * j + i] = code_times_scale(v - 3u * qd, s);
-                            v = qd;
-                        }
-                    }
-                } else {
-                    const uint8_t* p = packed + gn * row_bytes + g * (kGroup / 4) + part * 8;
-                    for (int j = 0; j < 8; ++j) {
-                        const uint32_t v = p[j];
-                        for (int i = 0; i < 4; ++i)
-                            dst[part * 32 + 4 * j + i] = code_times_scale((v >> (2 * i)) & 3u, s);
-                    }
-                }
-            } else {
-                for (int i = 0; i < 32; ++i) dst[part * 32 + i] = 0;
-            }
-        }
-        __syncthreads();
+        const uint32_t a_base = st0 + uint32_t(s) * kStage;
+        const uint32_t b_base = a_base + kAStage;
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            half8 a[2], b[2];
+        for (int ks = 0; ks < 2; ++ks) {
+            const int c = 4 * ks + (lane >> 4);
+            half8 af[4], bf[4];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int ra = wm + i * 16 + (lane & 15);
-                const int rb = wn + i * 16 + (lane & 15);
-                const int kk = ks + 8 * (lane >> 4);
-                a[i] = *reinterpret_cast<const half8*>(As + ra * kLdsStride + kk);
-                b[i] = *reinterpret_cast<const half8*>(Bs + rb * kLdsStride + kk);
+            for (int i = 0; i < 4; ++i) {
+                af[i] = __builtin_bit_cast(
+                    half8, *reinterpret_cast<lds_u32x4*>(a_base + swz(wm + 16 * i + (lane & 15), c)));
+                bf[i] = __builtin_bit_cast(
+                    half8, *reinterpret_cast<lds_u32x4*>(b_base + swz(wn + 16 * i + (lane & 15), c)));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        __syncthreads();
+        if (more) {
+            uint32_t v[16];
+            decode_b<FMT>(braw, t + 1, hh, rep, v);
+            store_b(v, s ^ 1);
+        }
+        vm_lds_barrier();
     }
 
     // lane holds D[4 * (lane / 16) + r][lane % 16] of each 16 x 16 tile
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t gm = m_base + wm + i * 16 + 4 * (lane >> 4) + r;
-                const int64_t gn = n_base + wn + j * 16 + (lane & 15);
-                if (gm < m && gn < n) {
+                const int64_t gm = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                const int64_t gcol = n0 + wn + 16 * j + (lane & 15);
+                if (gm < m && gcol < n) {
                     const float v = acc[i][j][r];
                     if (y_f16)
-                        reinterpret_cast<__half*>(y)[gm * n + gn] = __float2half_rn(v);
+                        reinterpret_cast<__half*>(y)[gm * n + gcol] = __float2half_rn(v);
                     else
-                        reinterpret_cast<float*>(y)[gm * n + gn] = v;
+                        reinterpret_cast<float*>(y)[gm * n + gcol] = v;
                 }
             }
+}
+
+template <int FMT>
+hipError_t launch(const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m,
+                  int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<FMT>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 lds_bytes<FMT>());
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t chunk = (tiles + 7) / 8;
+    hipLaunchKernelGGL(gemm_kernel<FMT>, dim3(unsigned(8 * chunk)), dim3(kThreads),
+                       size_t(lds_bytes<FMT>()), stream, packed, scales, x, m, n, k, y, y_f16,
+                       int(tiles_n), int(tiles), int(chunk));
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, const uint16_t* x,
                        int64_t m, int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
-    const dim3 grid(unsigned(((n + BN - 1) / BN) * ((m + BM - 1) / BM)));
-    if (fmt == 0)
-        hipLaunchKernelGGL(gemm_simple_kernel<0>, grid, dim3(kThreads), 0, stream, packed, scales,
-                           x, m, n, k, y, y_f16);
-    else
-        hipLaunchKernelGGL(gemm_simple_kernel<1>, grid, dim3(kThreads), 0, stream, packed, scales,
-                           x, m, n, k, y, y_f16);
-    return hipGetLastError();
+    return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
+                    : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
 }
 
 }  // namespace tl
