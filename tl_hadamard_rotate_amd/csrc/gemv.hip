@@ -95,6 +95,8 @@ __global__ __launch_bounds__(kThreads) void gemv_simple_kernel(
 
 hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt, const uint16_t* x,
                        int64_t m, int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    if (fmt == 1 && gemv_m1_slot2_fits(m, n, k))
+        return launch_gemv_m1_slot2(packed, scales, x, n, k, y, y_f16, stream);
     if (fmt == 1) return launch_gemv_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
     if (fmt == 0) return launch_gemv_trit5(packed, scales, x, m, n, k, y, y_f16, stream);
     const unsigned grid = unsigned((n + kWaves - 1) / kWaves);

@@ -23,6 +23,11 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt,
 hipError_t launch_gemv_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
+// M = 1 decode GEMV of the 2-bit-slot packing (matrix-core diagonal form);
+// usable when gemv_m1_slot2_fits(m, n, k)
+bool gemv_m1_slot2_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream);
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
