@@ -41,7 +41,7 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 STEP_LINEARS = ("gate", "up", "down")
 FMT_NAMES = {"trit5": 0, "slot2": 1}
-KERNEL_SRC = {0: "gemv.hip", 1: "gemv_slot2.hip"}
+KERNEL_SRC = {0: "gemv_trit5.hip", 1: "gemv_m1.hip"}
 
 
 def log(msg: str) -> None:
@@ -69,7 +69,7 @@ def source_sha(fmt: int) -> str:
 def traffic_from_profiles(fmt: int):
     """HBM bytes per GEMV launch from the committed counter summary, or None
     when there is none for the current kernel source."""
-    name = "gemv_slot2" if fmt == 1 else "gemv_trit5"
+    name = "gemv_m1_slot2" if fmt == 1 else "gemv_trit5"
     path = os.path.join(ROOT, "profiles", f"{name}_decode_mlp_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -171,27 +171,145 @@ def cpu_baseline(oracle, synth, fmt, budget_s=12.0, rows=512):
                       f"fp64 dequantised matrix-vector product), {passes} passes in {dt:.1f} s"}
 
 
-def bench_gemm(torch, tl, synth, dev, fmt, m=2048, reps=10):
-    """Prefill GEMM TFLOP/s at M=2048, K=5120, N=17408 (side figure)."""
-    k, n = synth.SHAPES["gate"]
-    inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=4)
-    packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
-    scales = torch.from_numpy(inp.scales).to(dev)
-    gen = torch.Generator(device="cpu").manual_seed(4)
-    x = torch.randn((m, k), generator=gen).to(torch.float16).to(dev)
-    y = torch.empty((m, n), dtype=torch.float32, device=dev)
-    tl.gemm(packed, scales, fmt, x, out=y)
-    torch.cuda.synchronize()
+def _event_time(torch, fn, reps):
+    """Milliseconds per call of fn() over `reps` calls, between HIP events on
+    torch's current stream (the stream the library launches on)."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(reps):
-        tl.gemm(packed, scales, fmt, x, out=y)
+    for i in range(reps):
+        fn(i)
     b.record()
     torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def bench_gemm(torch, tl, synth, dev, fmt, reps=5):
+    """Prefill GEMM TFLOP/s for M in {512, 2048, 4096} at the MLP shapes
+    (gate: K=5120 N=17408, down: K=17408 N=5120)."""
+    out = []
+    for name in ("gate", "down"):
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=synth.LINEAR_ID[name])
+        packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
+        scales = torch.from_numpy(inp.scales).to(dev)
+        for m in synth.PREFILL_M:
+            gen = torch.Generator(device="cpu").manual_seed(4 + m)
+            x = torch.randn((m, k), generator=gen).to(torch.float16).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            tl.gemm(packed, scales, fmt, x, out=y)
+            torch.cuda.synchronize()
+            ms = _event_time(torch, lambda i: tl.gemm(packed, scales, fmt, x, out=y), reps)
+            tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+            out.append({"linear": name, "M": m, "K": k, "N": n, "ms": round(ms, 4),
+                        "TFLOPs": round(tflops, 2),
+                        "frac_of_fp16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)})
+            del x, y
+        del packed, scales
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_batched(torch, tl, synth, dev, fmt, copies=20):
+    """Batched decode GEMV over one layer's attention projections q, k, v, o
+    at M in {1, 2, 4, 8, 16} (activations with 1% outliers x20); weights
+    cycled over `copies` distinct buffers (> the last-level cache)."""
+    out = []
+    for name in ("q", "k", "v", "o"):
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(n, k, 16, seed=0, cfg=3, linear=synth.LINEAR_ID[name],
+                                  outliers=True)
+        packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
+        scales = torch.from_numpy(inp.scales).to(dev)
+        packs = [packed] + [packed.clone() for _ in range(copies - 1)]
+        scs = [scales] + [scales.clone() for _ in range(copies - 1)]
+        signs = torch.from_numpy(inp.signs).to(dev)
+        x_rot = tl.hadamard_rotate(torch.from_numpy(inp.x).to(dev), signs)
+        for m in synth.BATCHED_M:
+            xm = x_rot[:m].contiguous()
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            for c in range(copies):
+                tl.gemv(packs[c], scs[c], fmt, xm, out=y)
+            torch.cuda.synchronize()
+            ms = _event_time(torch, lambda i: tl.gemv(packs[i % copies], scs[i % copies], fmt, xm,
+                                                      out=y), 3 * copies)
+            nbytes = gemv_bytes(n, k, m, fmt)
+            out.append({"linear": name, "M": m, "us": round(ms * 1e3, 3),
+                        "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del packs, scs
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_rotate_prefill(torch, tl, dev, reps=10):
+    """Activation rotation at prefill size M=4096, K in {5120, 17408}: GB/s of
+    the binary16 read + write."""
+    out = []
+    for k in (5120, 17408):
+        gen = torch.Generator(device="cpu").manual_seed(k)
+        x = torch.randn((4096, k), generator=gen).to(torch.float16).to(dev)
+        s = (torch.randint(0, 2, (k,), generator=gen) * 2 - 1).to(torch.int8).to(dev)
+        o = torch.empty_like(x)
+        tl.hadamard_rotate(x, s, out=o)
+        torch.cuda.synchronize()
+        ms = _event_time(torch, lambda i: tl.hadamard_rotate(x, s, out=o), reps)
+        out.append({"M": 4096, "K": k, "us": round(ms * 1e3, 2),
+                    "GBs": round(rotate_bytes(4096, k) / (ms * 1e-3) / 1e9, 1)})
+        del x, o
+    return out
+
+
+def bench_stream(torch, tl, synth, dev, fmt, stream, reps=5):
+    """The 27B-class weight stream at M=1: 64 layers x (q, k, v, o, gate, up,
+    down), each a rotation + GEMV, captured in one HIP graph per token.  One
+    layer is generated and replicated into 64 distinct device buffers (the
+    values do not change the streaming cost; distinct addresses defeat the
+    caches)."""
+    layer = []
+    for name in synth.LAYER_LINEARS:
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(n, k, 1, seed=0, cfg=5, layer=0, linear=synth.LINEAR_ID[name],
+                                  outliers=name in ("q", "k", "v", "o"))
+        layer.append((name, k, n, tl.pack(torch.from_numpy(inp.codes).to(dev), fmt),
+                      torch.from_numpy(inp.scales).to(dev), torch.from_numpy(inp.signs).to(dev),
+                      torch.from_numpy(inp.x).to(dev)))
+    lins = []
+    for li in range(synth.N_LAYERS):
+        for name, k, n, p, sc, sg, x in layer:
+            lins.append(dict(k=k, n=n, packed=p if li == 0 else p.clone(),
+                             scales=sc if li == 0 else sc.clone(), signs=sg, x=x,
+                             x_rot=torch.empty((1, k), dtype=torch.float16, device=dev),
+                             y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    weight_bytes = sum(l["packed"].numel() + l["scales"].numel() * 2 for l in lins)
+    act_bytes = sum(rotate_bytes(1, l["k"]) + 2 * l["k"] + 4 * l["n"] for l in lins)
+
+    def token():
+        for l in lins:
+            tl.hadamard_rotate(l["x"], l["signs"], out=l["x_rot"])
+            tl.gemv(l["packed"], l["scales"], fmt, l["x_rot"], out=l["y"])
+
+    with torch.cuda.stream(stream):
+        token()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            token()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
-    tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
-    return {"M": m, "K": k, "N": n, "ms": round(ms, 4), "TFLOPs": round(tflops, 2),
-            "frac_of_fp16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+    del g, lins, layer
+    torch.cuda.empty_cache()
+    return {"layers": synth.N_LAYERS, "linears_per_layer": len(synth.LAYER_LINEARS),
+            "launches_per_token": 2 * synth.N_LAYERS * len(synth.LAYER_LINEARS),
+            "weight_bytes": int(weight_bytes), "activation_bytes": int(act_bytes),
+            "ms_per_token": round(ms, 4), "weight_streams_per_s": round(1e3 / ms, 1),
+            "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
 
 
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
@@ -265,7 +383,7 @@ def main(argv=None) -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic),
-                "kernel": "tl_gemv (" + ("gemv_slot2_kernel" if fmt == 1 else "gemv_simple_kernel")
+                "kernel": "tl_gemv (" + ("gemv_m1_slot2_kernel" if fmt == 1 else "gemv_trit5_kernel")
                           + ")",
                 "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": round(per_launch)}
     log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; gemv avg {avg_us:.2f} us/launch, "
@@ -293,8 +411,14 @@ def main(argv=None) -> int:
             "gemv_GBs": round(b2 / (g2 * 1e-3 / (3 * reps)) / 1e9, 1)}
         del sg, gg, lins2
         torch.cuda.empty_cache()
-        log("prefill GEMM side figure")
+        log("prefill GEMM (M = 512, 2048, 4096)")
         extra["gemm_prefill"] = bench_gemm(torch, tl, synth, dev, fmt)
+        log("batched decode GEMV over q, k, v, o (M = 1..16)")
+        extra["batched_decode"] = bench_batched(torch, tl, synth, dev, fmt)
+        log("rotation at prefill size")
+        extra["rotate_prefill"] = bench_rotate_prefill(torch, tl, dev)
+        log("64-layer weight stream")
+        extra["weight_stream"] = bench_stream(torch, tl, synth, dev, fmt, stream)
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -128,6 +128,24 @@ TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t 
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
                   void* y, int32_t y_dtype, hipStream_t stream);
 
+/* The whole layer on unrotated activations:
+ *   x_rot = R(x)  (as tl_hadamard_rotate),   y = dequant(codes, scales) . x_rot
+ * i.e. y[m, n] = sum_k R(x)[m, k] * code[n, k] * scales[n, k/128]: the
+ * runtime rotation of the activations that the folded weights require (the
+ * Persian page, paragraphs 2 and 3) followed by the ternary product.
+ * x: binary16 [M, K], not rotated; signs: int8 [K]; x_rot: binary16 [M, K],
+ * caller-owned, receives R(x) (rounded to binary16 as tl_hadamard_rotate
+ * does); y as for tl_gemv.  Shape, format, dtype and alignment rules as
+ * tl_gemv (x in place of x_rot); x_rot must not overlap x, signs, packed,
+ * scales or y, and y must not overlap any input.  At M = 1 with
+ * TL_FMT_SLOT2 (and K <= 20480) the rotation runs inside the GEMV kernel: one
+ * launch, the rotated activations never make a round trip through memory
+ * before use (x_rot is still written).  Otherwise: tl_hadamard_rotate, then
+ * tl_gemv (M < 64) or tl_gemm (M >= 64). */
+TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                    const uint16_t* x, const int8_t* signs, int64_t M, int64_t N, int64_t K,
+                    uint16_t* x_rot, void* y, int32_t y_dtype, hipStream_t stream);
+
 /* Static name of a status code ("TL_OK", ...). */
 TL_API const char* tl_status_str(tl_status status);
 

@@ -77,6 +77,27 @@ def test_layer_validation(call):
     assert _gemv(fn, y=A + 16) == 5
 
 
+def test_linear_validation():
+    f = tl.lib().tl_linear
+    P, S, X, G, XR, Y = A, A + 0x1000000, A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x4000000
+
+    def call(packed=P, scales=S, fmt=1, x=X, signs=G, m=1, n=1024, k=1024, x_rot=XR, y=Y, yd=0):
+        return f(packed, scales, fmt, x, signs, m, n, k, x_rot, y, yd, NULL)
+
+    assert call(signs=NULL) == 1
+    assert call(x_rot=NULL) == 1
+    assert call(x=NULL) == 1
+    assert call(k=1000) == 2
+    assert call(fmt=4) == 3
+    assert call(signs=G + 4) == 4
+    assert call(x_rot=XR + 2) == 4
+    assert call(x_rot=X) == 5            # x_rot on top of x
+    assert call(x_rot=G - 16) == 5       # over the signs
+    assert call(x_rot=Y - 16) == 5       # into y
+    assert call(y=G) == 5                # y over the signs
+    assert call(yd=2) == 7
+
+
 def test_rotate_validation():
     f = tl.lib().tl_hadamard_rotate
     assert f(NULL, A, 1, 1024, A + 0x100000, NULL) == 1

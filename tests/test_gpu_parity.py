@@ -283,3 +283,52 @@ def test_full_size_decode_sampled_rows(gpu, fmt, shape):
     # against the binary16 rotated input the kernel actually read: tight
     want16 = oracle.matvec(inp.codes[rows], inp.scales[rows], host(x_rot))[0]
     assert oracle.rel_l2(y[rows], want16) < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# tl_linear: rotation + product in one call
+# ---------------------------------------------------------------------------
+
+def _rotation_bound_ok(got, want, x16):
+    """|got - want| within one binary16 rounding plus the fp32 error of a
+    10-level butterfly tree over the block (as in the rotation tests)."""
+    m, k = x16.shape
+    xa = np.abs(x16.astype(np.float64)).reshape(m, k // 1024, 1024).sum(-1) / 32.0
+    fp32_err = np.repeat(10 * 2.0 ** -24 * xa, 1024, axis=1)
+    half_ulp = 0.5 * np.maximum(oracle.fp16_ulp(got), oracle.fp16_ulp(want))
+    return np.all(np.abs(got - want) <= half_ulp + fp32_err)
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
+@pytest.mark.parametrize("m,n,k", [(1, 1024, 1024), (1, 333, 5120), (1, 2048, 17408),
+                                   (3, 700, 2048), (70, 200, 3072)])
+def test_linear_matches_oracle(gpu, fmt, m, n, k):
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=m + n + k, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), fmt)
+    scales = dev(inp.scales, gpu)
+    x_rot = torch.empty((m, k), dtype=torch.float16, device=gpu)
+    y = host(tl.linear(packed, scales, fmt, dev(inp.x, gpu), dev(inp.signs, gpu),
+                       x_rot=x_rot)).astype(np.float64)
+    xr = host(x_rot)
+    # the rotated activations it wrote: the rotation's own bound
+    assert _rotation_bound_ok(xr.astype(np.float64), oracle.rotate(inp.x, inp.signs), inp.x)
+    # the product is exactly the library's product on those activations
+    prod = tl.gemm if m >= 64 else tl.gemv
+    y2 = host(prod(packed, scales, fmt, x_rot)).astype(np.float64)
+    assert np.array_equal(y.astype(np.float32).view(np.uint32), y2.astype(np.float32).view(np.uint32))
+    # end to end against the fp64 layer
+    assert oracle.rel_l2(y, oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)) < 2e-3
+
+
+@pytest.mark.parametrize("shape", ["gate", "down", "k"])
+def test_linear_full_size_sampled_rows(gpu, shape):
+    """The fused M = 1 path at the 27B-class shapes; sampled rows against the
+    oracle's layer, with the rotation folded into the weights."""
+    k, n = synth.SHAPES[shape]
+    inp = synth.linear_inputs(n, k, 1, cfg=5, linear=synth.LINEAR_ID[shape])
+    packed = tl.pack(dev(inp.codes, gpu), tl.FMT_SLOT2)
+    y = host(tl.linear(packed, dev(inp.scales, gpu), tl.FMT_SLOT2, dev(inp.x, gpu),
+                       dev(inp.signs, gpu))).astype(np.float64)[0]
+    rows = np.concatenate([np.random.default_rng(1).choice(n, size=200, replace=False), [0, n - 1]])
+    want = oracle.linear(inp.x, inp.signs, inp.codes[rows], inp.scales[rows])[0]
+    assert oracle.rel_l2(y[rows], want) < 2e-3

@@ -56,6 +56,7 @@ def lib() -> ctypes.CDLL:
             "tl_hadamard_rotate": (i32, [p, p, i64, i64, p, p]),
             "tl_gemv": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
+            "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }
@@ -177,6 +178,43 @@ def gemm(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch
     return _linear("tl_gemm", packed, scales, fmt, x_rot, out_dtype, out)
 
 
+def linear(packed, scales, fmt, x, signs, out_dtype=torch.float32, out=None,
+           x_rot=None) -> torch.Tensor:
+    """y[M, N] = R(x) . dequant(codes, scales)^T on unrotated fp16 x [M, K];
+    x_rot (allocated when None) receives R(x).  One fused launch at M = 1
+    with the 2-bit-slot packing."""
+    _need(packed, "packed", torch.uint8, 2)
+    _need(scales, "scales", torch.float16, 2)
+    _need(x, "x", torch.float16, 2)
+    _need(signs, "signs", torch.int8, 1)
+    m, k = x.shape
+    n = packed.shape[0]
+    if signs.shape[0] != k:
+        raise ValueError("signs must have K entries")
+    if scales.shape != (n, k // GROUP):
+        raise ValueError(f"scales must be [N, K/128] = {(n, k // GROUP)}, got {tuple(scales.shape)}")
+    if packed.numel() != packed_bytes(n, k, fmt):
+        raise ValueError("packed size does not match N, K and the format")
+    if out_dtype not in (torch.float32, torch.float16):
+        raise TypeError("out_dtype must be float32 or float16")
+    if x_rot is None:
+        x_rot = torch.empty_like(x)
+    else:
+        _need(x_rot, "x_rot", torch.float16, 2)
+        if x_rot.shape != x.shape:
+            raise ValueError("x_rot must have the shape of x")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    else:
+        _need(out, "out", out_dtype, 2)
+        if out.shape != (m, n):
+            raise ValueError("out must be [M, N]")
+    yd = TL_F32 if out_dtype == torch.float32 else TL_F16
+    _check("tl_linear", lib().tl_linear(_ptr(packed), _ptr(scales), fmt, _ptr(x), _ptr(signs), m,
+                                        n, k, _ptr(x_rot), _ptr(out), yd, _stream(x)))
+    return out
+
+
 class TernaryLinear:
     """A ternary g128 linear layer whose weights carry the folded rotation.
 
@@ -189,9 +227,9 @@ class TernaryLinear:
         self.prefill_threshold = prefill_threshold
 
     def forward(self, x: torch.Tensor, out_dtype=torch.float32) -> torch.Tensor:
-        x_rot = hadamard_rotate(x, self.signs)
         if x.shape[0] >= self.prefill_threshold:
-            return gemm(self.packed, self.scales, self.fmt, x_rot, out_dtype)
-        return gemv(self.packed, self.scales, self.fmt, x_rot, out_dtype)
+            return gemm(self.packed, self.scales, self.fmt, hadamard_rotate(x, self.signs),
+                        out_dtype)
+        return linear(self.packed, self.scales, self.fmt, x, self.signs, out_dtype)
 
     __call__ = forward

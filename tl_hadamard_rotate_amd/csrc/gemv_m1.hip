@@ -201,6 +201,98 @@ __device__ void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t* img, u
     }
 }
 
+// Fused rotation (tl_linear).  Half-wave hw (32 lanes) rotates block hw:
+// lane j loads elements [32j, 32j + 32) and their signs, does the butterflies
+// of index bits 0-4 in registers, transposes through LDS (row stride 33
+// floats: conflict-free both ways), does bits 5-9 in registers, and writes
+// (1/32) * result, rounded once to binary16, to the block's activations in
+// LDS.  fp32 throughout, 10 butterfly levels per output, like
+// tl_hadamard_rotate (summation order differs, so results agree to within
+// that bound rather than bit for bit).
+constexpr int kRotScratch = 32 * 33 * 4;   // bytes of transpose scratch per block
+
+__device__ __forceinline__ void rot_load(const uint16_t* x, const int8_t* signs, int nb, int t,
+                                         uint4 (&xr)[4], uint4 (&sr)[2]) {
+    const int hw = t >> 5, j = t & 31;
+    if (hw < nb) {
+        const uint4* px = reinterpret_cast<const uint4*>(x + 1024 * hw + 32 * j);
+        const uint4* ps = reinterpret_cast<const uint4*>(signs + 1024 * hw + 32 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[i] = px[i];
+        sr[0] = ps[0];
+        sr[1] = ps[1];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xr[i] = uint4{0, 0, 0, 0};
+        sr[0] = sr[1] = uint4{0, 0, 0, 0};
+    }
+}
+
+template <int H>
+__device__ __forceinline__ void butterfly(float (&v)[32]) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        if (!(i & H)) {
+            const float a = v[i], b = v[i + H];
+            v[i] = a + b;
+            v[i + H] = a - b;
+        }
+}
+
+__device__ __forceinline__ void butterflies(float (&v)[32]) {
+    butterfly<1>(v);
+    butterfly<2>(v);
+    butterfly<4>(v);
+    butterfly<8>(v);
+    butterfly<16>(v);
+}
+
+__device__ void rot_run(const uint4 (&xr)[4], const uint4 (&sr)[2], int nb, int t, float* scratch,
+                        uint16_t* xrot) {
+    const int hw = t >> 5, j = t & 31;
+    if (hw >= nb) return;   // whole half-waves
+    const uint32_t xw[16] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w, xr[1].x, xr[1].y, xr[1].z, xr[1].w,
+                             xr[2].x, xr[2].y, xr[2].z, xr[2].w, xr[3].x, xr[3].y, xr[3].z, xr[3].w};
+    const uint32_t sw[8] = {sr[0].x, sr[0].y, sr[0].z, sr[0].w, sr[1].x, sr[1].y, sr[1].z, sr[1].w};
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        // a negative sign byte flips the sign bit of the fp32 value
+        const uint32_t neg = ((sw[i >> 2] >> (8 * (i & 3) + 7)) & 1u) << 31;
+        v[i] = __builtin_bit_cast(float,
+                                  __builtin_bit_cast(uint32_t, h2f((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) ^ neg);
+    }
+    butterflies(v);
+    float* row = scratch + hw * (32 * 33);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) row[j * 33 + i] = v[i];
+    // the same wave wrote the rows: its LDS operations complete in order
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = row[i * 33 + j];   // element 32 i + j
+    butterflies(v);
+    uint16_t* out = xrot + 1024 * hw + j;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) out[32 * i] = uint16_t(f2h(v[i] * 0.03125f));
+}
+
+// load_x from the rotated activations in LDS
+__device__ __forceinline__ void load_x_lds(const uint16_t* xrot, int nb, int t, uint4 (&raw)[4]) {
+    const int b = t >> 5;
+    const int u = img_u(t);
+    const int ep = img_ep(t);
+    if (t < nb * 32) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4* src = reinterpret_cast<const uint4*>(xrot + 1024 * b + eword_k(u, ep + 2 * h));
+            raw[2 * h] = src[0];
+            raw[2 * h + 1] = src[1];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = uint4{0, 0, 0, 0};
+    }
+}
+
 __device__ __forceinline__ half8 as_h8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
     return __builtin_bit_cast(half8, u32x4{a, b, c, d});
 }
@@ -219,14 +311,19 @@ __device__ __forceinline__ float pick(const float4v& d, int r) {
     return r == 0 ? d[0] : (r == 1 ? d[1] : (r == 2 ? d[2] : d[3]));
 }
 
-template <int FL>
+// ROT: x is the unrotated activations and signs their signs; the workgroup
+// rotates them in LDS first, and workgroup 0 also writes them to x_rot.
+template <int FL, bool ROT>
 __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
-    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t k, int row_base,
-    int row_rem, int rows_per_chunk, void* __restrict__ y, int y_f16) {
+    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, const int8_t* signs,
+    uint16_t* x_rot, int64_t k, int row_base, int row_rem, int rows_per_chunk,
+    void* __restrict__ y, int y_f16) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int nb = int(k / kBlock);
-    uint8_t* img = smem;
-    uint8_t* rec = smem + nb * kImgBlock;
+    // ROT: [rotated activations nb * 2 KB][transpose scratch, later the images ...]
+    uint16_t* xrot = reinterpret_cast<uint16_t*>(smem);
+    uint8_t* img = ROT ? smem + nb * 2048 : smem;
+    uint8_t* rec = img + nb * kImgBlock;
     float* red = reinterpret_cast<float*>(rec + nb * 4 * kRecBytes);
 
     const int tid = threadIdx.x;
@@ -365,16 +462,40 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     // weights.  Requested behind the whole weight stream, the activations
     // would arrive microseconds later.
     uint4 xraw[4];
-    load_x(x, nb, tid, xraw);
-    set_chunk(0);
-    issue(0, Zero{}, Head{});
-    // the empty asm keeps the image build below those weight loads
+    if constexpr (ROT) {
+        uint4 sr[2];
+        rot_load(x, signs, nb, tid, xraw, sr);
+        set_chunk(0);
+        issue(0, Zero{}, Head{});
+        // the empty asm keeps the rotation below those weight loads
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        asm volatile("" : "+v"(xraw[i].x), "+v"(xraw[i].y), "+v"(xraw[i].z), "+v"(xraw[i].w)
+        for (int i = 0; i < 4; ++i)
+            asm volatile("" : "+v"(xraw[i].x), "+v"(xraw[i].y), "+v"(xraw[i].z), "+v"(xraw[i].w)
+                         :
+                         : "memory");
+        asm volatile("" : "+v"(sr[0].x), "+v"(sr[0].y), "+v"(sr[0].z), "+v"(sr[0].w), "+v"(sr[1].x),
+                     "+v"(sr[1].y), "+v"(sr[1].z), "+v"(sr[1].w)
                      :
                      : "memory");
-    if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);   // nb * 32 <= kThreads
+        rot_run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), xrot);   // nb <= 32 half-waves
+        lds_barrier();
+        if (blockIdx.x == 0)
+            for (int i = tid; i < nb * 128; i += kThreads)
+                reinterpret_cast<uint4*>(x_rot)[i] = reinterpret_cast<const uint4*>(xrot)[i];
+        load_x_lds(xrot, nb, tid, xraw);
+        if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);
+    } else {
+        load_x(x, nb, tid, xraw);
+        set_chunk(0);
+        issue(0, Zero{}, Head{});
+        // the empty asm keeps the image build below those weight loads
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            asm volatile("" : "+v"(xraw[i].x), "+v"(xraw[i].y), "+v"(xraw[i].z), "+v"(xraw[i].w)
+                         :
+                         : "memory");
+        if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);   // nb * 32 <= kThreads
+    }
     lds_barrier();
     issue(0, Head{}, All{});
     run(0);
@@ -405,58 +526,106 @@ int num_cus() {
     return cus;
 }
 
-template <int FL>
+template <int FL, bool ROT>
 hipError_t launch_fl(unsigned grid, size_t lds, const uint8_t* packed, const uint16_t* scales,
-                     const uint16_t* x, int64_t n, int64_t k, int rpc, void* y, int y_f16,
-                     hipStream_t stream) {
+                     const uint16_t* x, const int8_t* signs, uint16_t* x_rot, int64_t n,
+                     int64_t k, int rpc, void* y, int y_f16, hipStream_t stream) {
     const int base = int(n / grid), rem = int(n % grid);
     static bool attr_set = false;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL>),
+            reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL, ROT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsLimit));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((gemv_m1_slot2_kernel<FL>), dim3(grid), dim3(kThreads), lds, stream, packed,
-                       scales, x, k, base, rem, rpc, y, y_f16);
+    hipLaunchKernelGGL((gemv_m1_slot2_kernel<FL, ROT>), dim3(grid), dim3(kThreads), lds, stream,
+                       packed, scales, x, signs, x_rot, k, base, rem, rpc, y, y_f16);
     return hipGetLastError();
 }
 
-}  // namespace
+struct M1Plan {
+    unsigned grid;
+    int rpc;       // rows per chunk
+    int steps;     // steps per slot and chunk
+    size_t lds;
+};
 
-bool gemv_m1_slot2_fits(int64_t m, int64_t n, int64_t k) {
+M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     const int64_t nb = k / kBlock;
-    const int64_t lds = nb * kImgBlock + nb * 4 * kRecBytes + int64_t(kMaxSegsPerChunk) * 16;
-    const int64_t grid = n < num_cus() ? n : num_cus();
-    const int64_t rows = (n + grid - 1) / grid;
-    // one image pass (32 threads per block) and 32-bit buffer offsets
-    return m == 1 && nb * 32 <= kThreads && lds <= int64_t(kLdsLimit) &&
-           rows * (k / 4) < (int64_t(1) << 31);
-}
-
-hipError_t launch_gemv_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
-                                int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
-    const int nb = int(k / kBlock);
     const int64_t grid = n < num_cus() ? n : num_cus();
     const int64_t rows = (n + grid - 1) / grid;                  // largest slice
     int64_t rpc = kMaxSegsPerChunk / nb;
     if (rpc < 1) rpc = 1;
     if (rpc > rows) rpc = rows;
-    const int64_t steps = (rpc * nb + kSlots - 1) / kSlots;      // per slot and chunk
-    const size_t lds = size_t(nb) * kImgBlock + size_t(nb) * 4 * kRecBytes + size_t(rpc * nb) * 16;
-    const unsigned g = unsigned(grid);
-    const int r = int(rpc);
-    switch (steps) {
-        case 1: return launch_fl<1>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 2: return launch_fl<2>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 3: return launch_fl<3>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 4: return launch_fl<4>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 5: return launch_fl<5>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 6: return launch_fl<6>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        case 7: return launch_fl<7>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
-        default: return launch_fl<8>(g, lds, packed, scales, x, n, k, r, y, y_f16, stream);
+    M1Plan p;
+    p.grid = unsigned(grid);
+    p.rpc = int(rpc);
+    p.steps = int((rpc * nb + kSlots - 1) / kSlots);
+    const size_t tail = size_t(nb) * kImgBlock + size_t(nb) * 4 * kRecBytes + size_t(rpc * nb) * 16;
+    p.lds = rot ? size_t(nb) * 2048 + (tail > size_t(nb) * kRotScratch ? tail : size_t(nb) * kRotScratch)
+                : tail;
+    return p;
+}
+
+template <bool ROT>
+hipError_t launch_m1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                     const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k, void* y, int y_f16,
+                     hipStream_t stream) {
+    const M1Plan p = m1_plan(n, k, ROT);
+    switch (p.steps) {
+        case 1:
+            return launch_fl<1, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 2:
+            return launch_fl<2, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 3:
+            return launch_fl<3, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 4:
+            return launch_fl<4, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 5:
+            return launch_fl<5, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 6:
+            return launch_fl<6, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        case 7:
+            return launch_fl<7, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
+        default:
+            return launch_fl<8, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+                                     y_f16, stream);
     }
+}
+
+bool m1_fits(int64_t m, int64_t n, int64_t k, bool rot) {
+    const int64_t nb = k / kBlock;
+    const int64_t grid = n < num_cus() ? n : num_cus();
+    const int64_t rows = (n + grid - 1) / grid;
+    // one image pass (32 threads per block, one half-wave per rotated block)
+    // and 32-bit buffer offsets
+    return m == 1 && nb * 32 <= kThreads && m1_plan(n, k, rot).lds <= kLdsLimit &&
+           rows * (k / 4) < (int64_t(1) << 31);
+}
+
+}  // namespace
+
+bool gemv_m1_slot2_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, k, false); }
+
+hipError_t launch_gemv_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    return launch_m1<false>(packed, scales, x, nullptr, nullptr, n, k, y, y_f16, stream);
+}
+
+bool linear_m1_slot2_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, k, true); }
+
+hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                  const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
+                                  void* y, int y_f16, hipStream_t stream) {
+    return launch_m1<true>(packed, scales, x, signs, x_rot, n, k, y, y_f16, stream);
 }
 
 }  // namespace tl

@@ -122,6 +122,30 @@ tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, co
         tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
 }
 
+tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x,
+                    const int8_t* signs, int64_t M, int64_t N, int64_t K, uint16_t* x_rot, void* y,
+                    int32_t y_dtype, hipStream_t stream) {
+    const tl_status st = check_layer(packed, scales, fmt, x, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    if (!signs || !x_rot) return TL_ERR_NULL;
+    if (!aligned16(signs) || !aligned16(x_rot)) return TL_ERR_ALIGN;
+    const int64_t xb = M * K * 2, yb = M * N * (y_dtype == TL_F32 ? 4 : 2);
+    if (overlap(x_rot, xb, x, xb) || overlap(x_rot, xb, signs, K) ||
+        overlap(x_rot, xb, packed, N * row_bytes(K, fmt)) ||
+        overlap(x_rot, xb, scales, N * (K / TL_GROUP) * 2) || overlap(x_rot, xb, y, yb) ||
+        overlap(y, yb, signs, K))
+        return TL_ERR_ALIAS;
+    const int y_f16 = y_dtype == TL_F16;
+    if (fmt == TL_FMT_SLOT2 && tl::linear_m1_slot2_fits(M, N, K))
+        return launched(
+            tl::launch_linear_m1_slot2(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
+    hipError_t e = tl::launch_hadamard(x, signs, M, K, x_rot, stream);
+    if (e != hipSuccess) return launched(e);
+    e = M >= 64 ? tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream)
+                : tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream);
+    return launched(e);
+}
+
 const char* tl_status_str(tl_status status) {
     switch (status) {
         case TL_OK: return "TL_OK";
