@@ -2,9 +2,10 @@
 
 A step is one decode pass (M = 1) over the 27B-class MLP projections
 gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120): for
-each projection the signed 1024-block Hadamard rotation of its input followed
-by the ternary GEMV (6 kernels).  Inputs are seeded synthetic tensors with the
-workload's distributions.
+each projection the signed 1024-block Hadamard rotation of its input and the
+ternary product (tl_linear: one fused kernel per projection with the 2-bit-slot
+packing, rotation + GEMV kernels with the dense trit packing).  Inputs are
+seeded synthetic tensors with the workload's distributions.
 
 Timing.  Each step is captured once in a HIP graph; the weights are replicated
 into --copies distinct buffers (one graph per copy) and the timed loop cycles
@@ -12,12 +13,16 @@ through them, so no step finds its weights in the 256 MB last-level cache.
 W warm-up steps, then exactly K timed steps between two HIP events on the
 launch stream, with a device synchronisation on both sides.
 
-The dominant kernel (the GEMV) is also timed on its own: a graph of the three
-GEMV launches per weight copy, replayed between HIP events on the same
-stream; the average launch duration gives the roofline figure.  HBM traffic of
-the GEMV comes from the rocprofv3 counter summary under profiles/, and is
-reported only while the kernel source is the one those counters were taken
-from.
+Dominant kernel (roofline): the fused tl_linear kernel, whose three launches
+make up the step (2-bit slots), or the GEMV timed on its own in a graph of
+three launches per weight copy (dense trits); average launch time between
+HIP events on the launch stream.  HBM traffic comes from the rocprofv3
+counter summary under profiles/ and is reported only while the kernel source
+is the one those counters were taken from.
+
+Extras: the other packing, the prefill GEMM sweep, batched decode over the
+attention projections, the rotation at prefill size, the 64-layer weight
+stream, and the CPU oracle on a bounded sample.
 
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
@@ -48,6 +53,14 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def linear_bytes(n: int, k: int, m: int, fmt: int) -> int:
+    """Algorithmic bytes of one fused tl_linear launch: codes + scales +
+    unrotated binary16 activations and int8 signs read, rotated activations
+    (binary16) and fp32 outputs written."""
+    code_bytes = n * (k // 128) * 26 if fmt == 0 else n * k // 4
+    return code_bytes + n * (k // 128) * 2 + m * k * 2 + k + m * k * 2 + m * n * 4
+
+
 def gemv_bytes(n: int, k: int, m: int, fmt: int) -> int:
     """Algorithmic bytes of one GEMV launch: packed codes + binary16 scales +
     binary16 activations read, fp32 outputs written."""
@@ -69,7 +82,7 @@ def source_sha(fmt: int) -> str:
 def traffic_from_profiles(fmt: int):
     """HBM bytes per GEMV launch from the committed counter summary, or None
     when there is none for the current kernel source."""
-    name = "gemv_m1_slot2" if fmt == 1 else "gemv_trit5"
+    name = "linear_m1_slot2" if fmt == 1 else "gemv_trit5"
     path = os.path.join(ROOT, "profiles", f"{name}_decode_mlp_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -101,12 +114,15 @@ def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
 
 
 def step_fn(tl, lins, fmt, c):
+    """One decode step: per projection, rotation + ternary product (tl_linear;
+    a single fused kernel at M=1 with the 2-bit-slot packing)."""
     for lin in lins:
-        tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
-        tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
+        tl.linear(lin["packs"][c], lin["scales"][c], fmt, lin["x"], lin["signs"],
+                  out=lin["y"], x_rot=lin["x_rot"])
 
 
 def gemv_fn(tl, lins, fmt, c):
+    """The products alone, on already rotated activations (tl_gemv)."""
     for lin in lins:
         tl.gemv(lin["packs"][c], lin["scales"][c], fmt, lin["x_rot"], out=lin["y"])
 
@@ -212,7 +228,8 @@ def bench_gemm(torch, tl, synth, dev, fmt, reps=5):
 def bench_batched(torch, tl, synth, dev, fmt, copies=20):
     """Batched decode GEMV over one layer's attention projections q, k, v, o
     at M in {1, 2, 4, 8, 16} (activations with 1% outliers x20); weights
-    cycled over `copies` distinct buffers (> the last-level cache)."""
+    cycled over `copies` distinct buffers (> the last-level cache), the
+    launches captured in one HIP graph (launch time per GEMV, gaps included)."""
     out = []
     for name in ("q", "k", "v", "o"):
         k, n = synth.SHAPES[name]
@@ -230,8 +247,14 @@ def bench_batched(torch, tl, synth, dev, fmt, copies=20):
             for c in range(copies):
                 tl.gemv(packs[c], scs[c], fmt, xm, out=y)
             torch.cuda.synchronize()
-            ms = _event_time(torch, lambda i: tl.gemv(packs[i % copies], scs[i % copies], fmt, xm,
-                                                      out=y), 3 * copies)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(copies):
+                    tl.gemv(packs[c], scs[c], fmt, xm, out=y)
+            g.replay()
+            torch.cuda.synchronize()
+            ms = _event_time(torch, lambda i: g.replay(), 3) / copies
+            del g
             nbytes = gemv_bytes(n, k, m, fmt)
             out.append({"linear": name, "M": m, "us": round(ms * 1e3, 3),
                         "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)})
@@ -284,8 +307,8 @@ def bench_stream(torch, tl, synth, dev, fmt, stream, reps=5):
 
     def token():
         for l in lins:
-            tl.hadamard_rotate(l["x"], l["signs"], out=l["x_rot"])
-            tl.gemv(l["packed"], l["scales"], fmt, l["x_rot"], out=l["y"])
+            tl.linear(l["packed"], l["scales"], fmt, l["x"], l["signs"], out=l["y"],
+                      x_rot=l["x_rot"])
 
     with torch.cuda.stream(stream):
         token()
@@ -306,7 +329,7 @@ def bench_stream(torch, tl, synth, dev, fmt, stream, reps=5):
     del g, lins, layer
     torch.cuda.empty_cache()
     return {"layers": synth.N_LAYERS, "linears_per_layer": len(synth.LAYER_LINEARS),
-            "launches_per_token": 2 * synth.N_LAYERS * len(synth.LAYER_LINEARS),
+            "linear_calls_per_token": synth.N_LAYERS * len(synth.LAYER_LINEARS),
             "weight_bytes": int(weight_bytes), "activation_bytes": int(act_bytes),
             "ms_per_token": round(ms, 4), "weight_streams_per_s": round(1e3 / ms, 1),
             "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
@@ -314,8 +337,8 @@ def bench_stream(torch, tl, synth, dev, fmt, stream, reps=5):
 
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
-    256 MiB written per launch) and the step's GEMVs (10 launches per shape,
-    weights cycled over 8 copies)."""
+    256 MiB written per launch), then 10 eager decode steps (per projection
+    tl_linear, and tl_gemv alone), weights cycled over 8 copies."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -326,6 +349,7 @@ def profile_pass(torch, tl, synth, dev, fmt) -> int:
     for lin in lins:
         tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
     for i in range(10):
+        step_fn(tl, lins, fmt, i % 8)
         gemv_fn(tl, lins, fmt, i % 8)
     torch.cuda.synchronize()
     log("profile pass done")
@@ -372,25 +396,32 @@ def main(argv=None) -> int:
     sbytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
     value = sbytes / (ms * 1e-3) / 1e9
 
-    # dominant kernel: the GEMV, timed alone (3 launches per replay)
+    # the products alone on rotated activations (tl_gemv, 3 launches per replay)
     reps = max(args.steps, 3 * args.copies)
     g_ms = timed_replays(torch, gemv_graphs, reps, args.warmup, stream)
-    launches = 3 * reps
-    avg_us = g_ms * 1e3 / launches
-    per_launch = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+    g_us = g_ms * 1e3 / (3 * reps)
+    g_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+    # dominant kernel: with the 2-bit-slot packing the step is three launches
+    # of the fused rotate + GEMV kernel, so the step replays time it directly;
+    # otherwise it is the GEMV, timed alone
+    if fmt == 1:
+        avg_us = ms * 1e3 / 3.0
+        per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+        kname = "tl_linear (gemv_m1_slot2_kernel, rotation fused)"
+    else:
+        avg_us, per_launch, kname = g_us, g_bytes, "tl_gemv (gemv_trit5_kernel)"
     achieved = per_launch / (avg_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(fmt)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None if traffic is None else round(traffic),
-                "kernel": "tl_gemv (" + ("gemv_m1_slot2_kernel" if fmt == 1 else "gemv_trit5_kernel")
-                          + ")",
+                "traffic": None if traffic is None else round(traffic), "kernel": kname,
                 "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": round(per_launch)}
-    log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; gemv avg {avg_us:.2f} us/launch, "
-        f"{achieved:.1f} GB/s")
+    log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; dominant kernel avg {avg_us:.2f} us/launch, "
+        f"{achieved:.1f} GB/s; gemv alone {g_us:.2f} us/launch")
     del step_graphs, gemv_graphs
 
-    extra = {}
+    extra = {"gemv_alone": {"avg_launch_us": round(g_us, 3),
+                            "GBs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)}}
     if not args.no_extra:
         other = 1 - fmt
         del lins
@@ -434,7 +465,8 @@ def main(argv=None) -> int:
         "config": {"workload": "decode step M=1 over 27B-class MLP projections gate/up "
                                "(K=5120, N=17408) and down (K=17408, N=5120): signed "
                                "1024-block Hadamard rotation + ternary g128 GEMV per "
-                               "projection; binary16 activations, fp32 accumulation",
+                               "projection (tl_linear); binary16 activations, fp32 "
+                               "accumulation",
                    "format": args.fmt, "M": 1, "weight_copies": args.copies,
                    "step_bytes": sbytes},
         "roofline": roofline,

@@ -453,11 +453,11 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     };
 
     using Zero = std::integral_constant<int, 0>;
-    using Head = std::integral_constant<int, 1>;
+    using Head = std::integral_constant<int, (2 < FL ? 2 : FL)>;
     using All = std::integral_constant<int, FL>;
     // Prologue.  The activations are needed first and every workgroup reads
     // them, so they are requested ahead of the weight stream: the loads of the
-    // activations, then the first step's weights, then the activation images
+    // activations, then the first two steps' weights, then the activation images
     // (built by the waves that hold activations), then the rest of the
     // weights.  Requested behind the whole weight stream, the activations
     // would arrive microseconds later.
