@@ -8,13 +8,12 @@
 //
 // Tiling: a workgroup of 8 waves computes a 128 x 256 output tile (M x N);
 // wave w owns the 64 x 64 sub-tile (w / 4, w % 4), 4 x 4 MFMA tiles.  K runs in
-// steps of BK = 64 through two LDS stages:
-//   - activations: copied global -> LDS by direct loads (1 KB per wave
-//     instruction), no registers involved;
-//   - weights: the packed bytes of the next step are loaded into registers,
-//     decoded through a small LDS table, multiplied by their scale (packed
-//     fp16) and written to the other stage while the current step's MFMAs run;
-//   - one barrier per K step.
+// steps of BK = 64 through two LDS stages.  Global loads (activations and
+// packed weights) run four steps ahead in a ring of registers, so that their
+// latency (an L2 or HBM round trip under load) overlaps four steps of MFMAs;
+// during step t the MFMAs read stage t % 2 while step t + 1 is written to the
+// other stage (activations as loaded, weights decoded through a small LDS
+// table and multiplied by their scale in packed fp16); one barrier per step.
 // Both tiles are stored [row][64 halves] with the 16-byte chunks of row r
 // permuted by c -> c ^ ((r >> 1) & 7), so that the 16 lanes a 128-bit LDS read
 // serves per cycle (16 rows, one chunk) hit 16 distinct bank groups.
@@ -22,6 +21,8 @@
 // of tiles, N fastest: concurrent workgroups of an XCD share activation rows
 // in that XCD's L2.
 #include <hip/hip_fp16.h>
+
+#include <type_traits>
 
 #include "tl_internal.h"
 
@@ -55,29 +56,6 @@ constexpr int lds_bytes() { return lut_bytes<FMT>() + 2 * kStage; }
 // byte offset of 16-byte chunk c of row r in a [rows][64 halves] tile
 __device__ __forceinline__ uint32_t swz(int r, int c) {
     return uint32_t(r) * 128u + 16u * uint32_t(c ^ ((r >> 1) & 7));
-}
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// Copy 1 KB (16 bytes per lane) from global memory straight into LDS at the
-// wave-uniform byte offset lds_off.  Issued from asm so that the compiler does
-// not track it; completion is covered by the wait in vm_lds_barrier.  No
-// register is written.
-__device__ __forceinline__ void dma_1k(uint32_t lds_off, const void* src) {
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off"
-        :
-        : "s"(lds_off), "v"(src)
-        : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-__device__ __forceinline__ void vm_lds_barrier() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" : : : "memory");
-    __builtin_amdgcn_sched_barrier(0);
 }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -124,7 +102,9 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t codes, half2v s2) {
 // Packed bytes of one K step for this thread's weight row and half (32 codes).
 struct BRaw {
     uint32_t d[7];    // TRIT5: the group's 26 bytes from byte (26g & 3); SLOT2: d[0..1]
-    uint16_t s;       // the row's scale for this step's group
+    uint32_t s;       // the row's scales of groups (g & ~1, g | 1): a whole
+                      // register, so a load into one ring slot never waits on
+                      // a register shared with another
 };
 
 template <int FMT>
@@ -143,7 +123,7 @@ __device__ __forceinline__ void load_b(BRaw& r, const uint8_t* prow, const uint1
         r.d[0] = v.x;
         r.d[1] = v.y;
     }
-    r.s = srow[g];
+    r.s = *reinterpret_cast<const uint32_t*>(srow + (g & ~1));   // rows hold 8k groups
 }
 
 // LDS address of the table entry for the byte at bit position `shift` of
@@ -188,7 +168,8 @@ __device__ __forceinline__ void decode_t5(const BRaw& r, uint32_t rep, half2v s2
 template <int FMT>
 __device__ __forceinline__ void decode_b(const BRaw& r, int t, int hh, uint32_t rep,
                                          uint32_t (&out)[16]) {
-    const half2v s2 = half2v{__builtin_bit_cast(_Float16, r.s), __builtin_bit_cast(_Float16, r.s)};
+    const uint16_t sh = uint16_t(r.s >> (16 * ((t >> 1) & 1)));   // wave-uniform select
+    const half2v s2 = half2v{__builtin_bit_cast(_Float16, sh), __builtin_bit_cast(_Float16, sh)};
     if (FMT == 1) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -213,6 +194,12 @@ __device__ __forceinline__ void decode_b(const BRaw& r, int t, int hh, uint32_t 
         }
     }
 }
+
+// Activations of one K step for this thread: row ar of the tile, 16-byte
+// chunks ac and ac + 1 (32 contiguous bytes; four threads per 128-byte row).
+struct ARaw {
+    uint4 v[2];
+};
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
@@ -244,26 +231,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint16_t* srow = scales + gn * groups;
     const uint32_t rep = lds0 + uint32_t(lane & (kCopies - 1)) * uint32_t(entry_bytes<FMT>());
 
-    // activation rows of this thread's DMA lanes: wave w copies 1 KB pieces w
-    // and w + 8 of the 16 KB A stage; piece i = rows 8i..8i+7, lane l -> row
-    // 8i + l/8, physical chunk l % 8 holding logical chunk (l%8) ^ ((row>>1)&7)
-    const uint16_t* a_src[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = 8 * (wave + 8 * h) + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
-        const int64_t gm = m0 + r < m ? m0 + r : m - 1;        // rows past M copy row M-1
-        a_src[h] = x + gm * k + 8 * c;
-    }
+    // activation row and chunks of this thread
+    const int ar = tid >> 2, ac = 2 * (tid & 3);
+    const int64_t gm = m0 + ar < m ? m0 + ar : m - 1;          // rows past M copy row M-1
+    const uint16_t* asrc = x + gm * k + 8 * ac;
 
-    build_lut<FMT>(smem, tid);
-
-    auto issue_a = [&](int t, int s) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            dma_1k(st0 + uint32_t(s) * kStage + 1024u * uint32_t(wave + 8 * h), a_src[h] + BK * t);
+    auto load_a = [&](ARaw& a, int t) {
+        const uint4* p = reinterpret_cast<const uint4*>(asrc + BK * t);
+        a.v[0] = p[0];
+        a.v[1] = p[1];
     };
-    auto store_b = [&](const uint32_t (&v)[16], int s) {
+    auto store_a = [&](const ARaw& a, int s) {
+        const uint32_t base = st0 + uint32_t(s) * kStage;
+        *reinterpret_cast<lds_u32x4*>(base + swz(ar, ac)) = __builtin_bit_cast(u32x4, a.v[0]);
+        *reinterpret_cast<lds_u32x4*>(base + swz(ar, ac + 1)) = __builtin_bit_cast(u32x4, a.v[1]);
+    };
+    auto store_b = [&](const BRaw& r, int t, int s) {
+        uint32_t v[16];
+        decode_b<FMT>(r, t, hh, rep, v);
         const uint32_t base = st0 + uint32_t(s) * kStage + kAStage;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -271,17 +256,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                 u32x4{v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3]};
     };
 
-    // prologue: step 0 into stage 0
-    BRaw braw;
-    issue_a(0, 0);
-    load_b<FMT>(braw, prow, srow, 0);
-    lds_barrier();   // the decode table
-    {
-        uint32_t v[16];
-        decode_b<FMT>(braw, 0, hh, rep, v);
-        store_b(v, 0);
+    // Loads run four K steps ahead of their use: step j's raw activations and
+    // packed weights sit in ring slot j % 4 until they are written to LDS (the
+    // weights decoded) during step j - 1.  K is a multiple of 1024, so the
+    // number of steps is a multiple of 16 and the loop below needs no tail;
+    // loads past the last step re-read the last step (no branch around any
+    // load, so every wait the compiler places is exact).
+    ARaw ra[4];
+    BRaw rb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        load_a(ra[i], i);
+        load_b<FMT>(rb[i], prow, srow, i);
     }
-    vm_lds_barrier();
+    build_lut<FMT>(smem, tid);
+    lds_barrier();   // the decode table
+    store_a(ra[0], 0);
+    store_b(rb[0], 0, 0);
+    load_a(ra[0], 4);
+    load_b<FMT>(rb[0], prow, srow, 4);
+    lds_barrier();
 
     const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
     float4v acc[4][4];
@@ -290,13 +284,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    for (int t = 0; t < ksteps; ++t) {
+    // one K step: MFMAs on stage t & 1, then step t + 1 (ring slot SLOT) to
+    // the other stage and step t + 5 loaded into that slot
+    auto step = [&](int t, auto slot_c) {
+        constexpr int SLOT = decltype(slot_c)::value;
         const int s = t & 1;
-        const bool more = t + 1 < ksteps;
-        if (more) {
-            issue_a(t + 1, s ^ 1);
-            load_b<FMT>(braw, prow, srow, t + 1);
-        }
         const uint32_t a_base = st0 + uint32_t(s) * kStage;
         const uint32_t b_base = a_base + kAStage;
 #pragma unroll
@@ -316,12 +308,24 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if (more) {
-            uint32_t v[16];
-            decode_b<FMT>(braw, t + 1, hh, rep, v);
-            store_b(v, s ^ 1);
-        }
-        vm_lds_barrier();
+        // after the last step this writes a stage nobody reads
+        const int t1 = t + 1 < ksteps ? t + 1 : ksteps - 1;
+        store_a(ra[SLOT], s ^ 1);
+        store_b(rb[SLOT], t1, s ^ 1);
+        const int t5 = t + 5 < ksteps ? t + 5 : ksteps - 1;
+        load_a(ra[SLOT], t5);
+        load_b<FMT>(rb[SLOT], prow, srow, t5);
+        lds_barrier();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    for (int t = 0; t < ksteps; t += 4) {   // step t + 1 is in slot (t + 1) % 4
+        step(t, S1{});
+        step(t + 1, S2{});
+        step(t + 2, S3{});
+        step(t + 3, S0{});
     }
 
     // lane holds D[4 * (lane / 16) + r][lane % 16] of each 16 x 16 tile
@@ -331,14 +335,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t gm = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
+                const int64_t gm2 = m0 + wm + 16 * i + 4 * (lane >> 4) + r;
                 const int64_t gcol = n0 + wn + 16 * j + (lane & 15);
-                if (gm < m && gcol < n) {
+                if (gm2 < m && gcol < n) {
                     const float v = acc[i][j][r];
                     if (y_f16)
-                        reinterpret_cast<__half*>(y)[gm * n + gcol] = __float2half_rn(v);
+                        reinterpret_cast<__half*>(y)[gm2 * n + gcol] = __float2half_rn(v);
                     else
-                        reinterpret_cast<float*>(y)[gm * n + gcol] = v;
+                        reinterpret_cast<float*>(y)[gm2 * n + gcol] = v;
                 }
             }
 }
@@ -367,6 +371,7 @@ hipError_t launch(const uint8_t* packed, const uint16_t* scales, const uint16_t*
 
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, const uint16_t* x,
                        int64_t m, int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    if (m < 1 || n < 1 || k < 1024 || k % 1024 != 0) return hipErrorInvalidValue;   // see the loop
     return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
                     : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
 }
