@@ -43,15 +43,20 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kAStage = BM * BK * 2;          // 16 KB
 constexpr int kBStage = BN * BK * 2;          // 32 KB
 constexpr int kStage = kAStage + kBStage;
-constexpr int kCopies = 8;                    // decode-table copies (bank spread)
 // decode table: TRIT5 entry = five codes in 16 bytes, SLOT2 entry = four codes
-// in 8 bytes; copy c of entry v at v * (kCopies * entry) + c * entry
+// in 8 bytes; copy c of entry v at v * (copies * entry) + c * entry.  Lane l
+// reads copy l % copies, so the lanes one LDS cycle serves (256 bytes: 16
+// lanes of 16-byte reads, 32 lanes of 8-byte reads) never share a bank,
+// whatever bytes they look up.
 template <int FMT>
 constexpr int entry_bytes() { return FMT == 0 ? 16 : 8; }
 template <int FMT>
-constexpr int lut_bytes() { return 256 * kCopies * entry_bytes<FMT>(); }
+constexpr int copies() { return FMT == 0 ? 16 : 32; }
+template <int FMT>
+constexpr int lut_bytes() { return 256 * copies<FMT>() * entry_bytes<FMT>(); }   // 64 KB
 template <int FMT>
 constexpr int lds_bytes() { return lut_bytes<FMT>() + 2 * kStage; }
+static_assert(lds_bytes<0>() <= 160 * 1024 && lds_bytes<1>() <= 160 * 1024, "LDS");
 
 // byte offset of 16-byte chunk c of row r in a [rows][64 halves] tile
 __device__ __forceinline__ uint32_t swz(int r, int c) {
@@ -73,7 +78,7 @@ template <int FMT>
 __device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
     for (int c = tid; c < lut_bytes<FMT>() / 16; c += kThreads) {
         if (FMT == 0) {
-            const uint32_t v = uint32_t(c) / kCopies;       // one 16-byte entry per piece
+            const uint32_t v = uint32_t(c) / copies<FMT>();   // one 16-byte entry per piece
             uint32_t h[5] = {0, 0, 0, 0, 0};
             if (v < 243) {
                 uint32_t r = v;
@@ -86,7 +91,7 @@ __device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
             reinterpret_cast<uint4*>(lut)[c] =
                 uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
         } else {
-            const uint32_t v = uint32_t(c) / (kCopies / 2);   // two 8-byte copies per piece
+            const uint32_t v = uint32_t(c) / (copies<FMT>() / 2);   // two 8-byte copies per piece
             const uint32_t lo = code_bits(v & 3u) | (code_bits((v >> 2) & 3u) << 16);
             const uint32_t hi = code_bits((v >> 4) & 3u) | (code_bits((v >> 6) & 3u) << 16);
             reinterpret_cast<uint4*>(lut)[c] = uint4{lo, hi, lo, hi};
@@ -130,7 +135,7 @@ __device__ __forceinline__ void load_b(BRaw& r, const uint8_t* prow, const uint1
 // word w, in this lane's copy (rep = table base + copy offset)
 template <int FMT>
 __device__ __forceinline__ uint32_t lut_off(uint32_t w, int shift, uint32_t rep) {
-    return __builtin_amdgcn_ubfe(w, shift, 8) * uint32_t(kCopies * entry_bytes<FMT>()) + rep;
+    return __builtin_amdgcn_ubfe(w, shift, 8) * uint32_t(copies<FMT>() * entry_bytes<FMT>()) + rep;
 }
 
 // TRIT5: codes (c, c + 1) of a group from the entries of the byte holding c
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const int64_t gn = n0 + b_row < n ? n0 + b_row : n - 1;   // rows past N decode row N-1
     const uint8_t* prow = packed + gn * row_bytes + (FMT == 1 ? 8 * hh : 0);
     const uint16_t* srow = scales + gn * groups;
-    const uint32_t rep = lds0 + uint32_t(lane & (kCopies - 1)) * uint32_t(entry_bytes<FMT>());
+    const uint32_t rep = lds0 + uint32_t(lane & (copies<FMT>() - 1)) * uint32_t(entry_bytes<FMT>());
 
     // activation row and chunks of this thread
     const int ar = tid >> 2, ac = 2 * (tid & 3);
@@ -372,6 +377,8 @@ hipError_t launch(const uint8_t* packed, const uint16_t* scales, const uint16_t*
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, const uint16_t* x,
                        int64_t m, int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
     if (m < 1 || n < 1 || k < 1024 || k % 1024 != 0) return hipErrorInvalidValue;   // see the loop
+    if (fmt == 1 && gemm_slot2_fits(m, n, k))
+        return launch_gemm_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
     return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
                     : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
 }

@@ -37,6 +37,12 @@ hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales,
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
+// Prefill GEMM of the 2-bit-slot packing with the weights decoded in
+// registers; usable when gemm_slot2_fits(m, n, k)
+bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                             int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                             hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, hipStream_t stream);
