@@ -41,7 +41,10 @@
 // workgroups of an XCD share activation rows in that XCD's L2.
 #include <hip/hip_fp16.h>
 
+#include <map>
+#include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "tl_internal.h"
 
@@ -60,6 +63,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kAStage = BM * BK * 2;   // 32 KB
 constexpr int kStages = 4;
+constexpr int kTileFloats = BM * BN;   // partial sums of one tile
 constexpr int kBStage = BN * 16;     // 4 KB: packed weights of one step
 constexpr int kSStage = BN * 4;      // 1 KB: scales of one block
 constexpr int kLds = kStages * (kAStage + kBStage) + 2 * kSStage;   // 146 KB
@@ -98,13 +102,30 @@ __device__ __forceinline__ void decode8(uint32_t w, int h, ScaleSel sc, uint32_t
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m, int64_t n,
-    int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int chunk) {
+    int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int t0, int chunk_a,
+    int splits, int chunk_b, float* __restrict__ ws) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t st0 = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(smem)));
 
-    // XCD-aware tile order: XCD (blockIdx % 8) takes tiles [xcd * chunk, ...)
-    const int tile = int(blockIdx.x & 7) * chunk + int(blockIdx.x >> 3);
-    if (tile >= tiles) return;
+    // Work items.  Tiles [0, t0) are computed whole by blocks [0, 8 chunk_a);
+    // each tile of [t0, tiles) is split along K into `splits` parts, item v of
+    // blocks [8 chunk_a, ...) being part v % splits of tile t0 + v / splits.
+    // XCD-aware order in both ranges: XCD (blockIdx % 8) takes a contiguous
+    // run of items, N fastest, so that concurrent workgroups of an XCD share
+    // activation rows (and the parts of a tile sit on one XCD).
+    int tile, sp = 0, slot = 0;
+    bool split = false;
+    if (int(blockIdx.x) < 8 * chunk_a) {
+        tile = int(blockIdx.x & 7) * chunk_a + int(blockIdx.x >> 3);
+        if (tile >= t0) return;
+    } else {
+        const int u = int(blockIdx.x) - 8 * chunk_a;
+        slot = (u & 7) * chunk_b + (u >> 3);
+        if (slot >= (tiles - t0) * splits) return;
+        tile = t0 + slot / splits;
+        sp = slot % splits;
+        split = splits > 1;
+    }
     const int64_t m0 = int64_t(tile / tiles_n) * BM;
     const int64_t n0 = int64_t(tile % tiles_n) * BN;
 
@@ -113,6 +134,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nblk = int(k / 256);
     const int ksteps = 4 * nblk;
+    // K range of this item, in units of 8 steps (the loop's unroll)
+    const int units = nblk / 2;
+    const int u0 = split ? sp * units / splits : 0, u1 = split ? (sp + 1) * units / splits : units;
+    const int tb = 8 * u0;   // first step
     const uint32_t groups = uint32_t(k / kGroup);
     const uint32_t row_bytes = uint32_t(k / 4);
 
@@ -219,11 +244,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dma_a(stg_a[i], i, u);
+        for (int u = 0; u < 8; ++u) dma_a(stg_a[i], tb + i, u);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dma_b(stg_b[i], i, v);
+        for (int v = 0; v < 4; ++v) dma_b(stg_b[i], tb + i, v);
     }
-    dma_s(stg_s[0], 0);
+    dma_s(stg_s[0], tb >> 2);
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
     __builtin_amdgcn_sched_barrier(0);
@@ -345,6 +370,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bf[s & 1][j], acc[i][j],
                                                                        0, 0, 0);
+#ifdef TL_GEMM_SCHED
+            // next slice's LDS reads first, then each MFMA followed by a few
+            // VALU operations of the next slice's decode
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, TL_GEMM_SCHED, 0);
+            }
+#endif
+#ifdef TL_GEMM_KEEP
+            // this slice's operands stay allocated to the end of the slice, so
+            // the next decode never writes a register an MFMA in flight reads
+            asm volatile("" ::"v"(af[s & 1][0]), "v"(af[s & 1][1]), "v"(af[s & 1][2]), "v"(af[s & 1][3]),
+                         "v"(bf[s & 1][0]), "v"(bf[s & 1][1]), "v"(bf[s & 1][2]), "v"(bf[s & 1][3]));
+#endif
         }
         {   // rotate the stages
             const uint32_t a0 = stg_a[0];
@@ -376,9 +417,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         step(t + 2, C2{}, tb_c);
         step(t + 3, C3{}, tb_c);
     };
-    for (int t_blk = 0; t_blk < nblk; t_blk += 2) {   // nblk is a multiple of 4
+    for (int t_blk = 2 * u0; t_blk < 2 * u1; t_blk += 2) {
         block(t_blk, C0{});
         block(t_blk + 1, C1{});
+    }
+
+    // loads into stages nobody reads may still be in flight: drain them before
+    // the workgroup can end and its LDS be handed to another
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+
+    if (split) {
+        // part of a K-split tile: its partial sums go to this item's
+        // workspace slot, [register][thread]; gemm_slot2_reduce adds the parts
+        float* mine = ws + size_t(slot) * kTileFloats;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mine[((i * 4 + j) * 16 + r) * kThreads + tid] = acc[i][j][r];
+        return;
     }
 
     // lane holds D[8 * (r / 4) + 4 * (lane / 32) + r % 4][lane % 32] of each
@@ -401,6 +459,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
 }
 
+// Sum of the K parts of the split tiles, in part order (so the result does
+// not depend on the order the parts ran in), stored to y.  Block b handles
+// register e = b % 256 of split tile t0 + b / 256 for all 256 threads of the
+// GEMM's workgroup layout: thread tid holds that register of wave tid / 64 at
+// the same place as there.
+__global__ __launch_bounds__(kThreads) void gemm_slot2_reduce(const float* __restrict__ ws,
+                                                              int64_t m, int64_t n, void* __restrict__ y,
+                                                              int y_f16, int tiles_n, int t0, int splits) {
+    const int tt = int(blockIdx.x >> 8), e = int(blockIdx.x & 255);
+    const int tile = t0 + tt;
+    const int64_t m0 = int64_t(tile / tiles_n) * BM;
+    const int64_t n0 = int64_t(tile % tiles_n) * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128, q = lane >> 5;
+    const float* parts = ws + size_t(tt) * splits * kTileFloats + e * kThreads + tid;
+    float sum = parts[0];
+    for (int p = 1; p < splits; ++p) sum += parts[size_t(p) * kTileFloats];
+    const int i = e >> 6, j = (e >> 4) & 3, r = e & 15;
+    const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
+    const int64_t col = n0 + wn + 32 * j + (lane & 31);
+    if (row < m && col < n) {
+        if (y_f16)
+            reinterpret_cast<__half*>(y)[row * n + col] = __float2half_rn(sum);
+        else
+            reinterpret_cast<float*>(y)[row * n + col] = sum;
+    }
+}
+
 }  // namespace
 
 bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k) {
@@ -408,6 +494,75 @@ bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k) {
     return m >= 1 && n >= 1 && k >= 1024 && k % 1024 == 0 && m * k < (int64_t(1) << 31) &&
            n * (k / 4) < (int64_t(1) << 32);
 }
+
+namespace {
+
+// K split of the tiles that do not fill a whole round of workgroups (one per
+// CU).  Cost model in units of the loop (8 steps, about 14 us of one
+// workgroup): rounds of parts of ceil(units / splits) units, plus the partial
+// sums written and read back (512 KB per part, about 0.01 unit at the HBM
+// rate) and the reducing launch (0.3 unit).
+struct Plan {
+    int t0, splits;
+};
+
+Plan plan_split(int64_t tiles, int units, int cus) {
+    const int64_t rem = tiles % cus;
+    Plan best{int(tiles), 1};
+    if (rem == 0) return best;
+    double best_cost = units;
+    for (int s = 2; s <= 16 && s <= units; ++s) {
+        const int64_t rounds = (rem * s + cus - 1) / cus;
+        const double cost = double(rounds) * double((units + s - 1) / s) + 0.01 * double(rem * s) + 0.3;
+        if (cost < best_cost - 0.5) {
+            best_cost = cost;
+            best = Plan{int(tiles - rem), s};
+        }
+    }
+    return best;
+}
+
+// Partial-sum workspace, one per (device, stream), so that launches that may
+// overlap never share one; grown on demand (hipMalloc: such a call cannot be
+// captured into a graph), never shrunk.
+struct Workspace {
+    float* ws = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+hipError_t get_workspace(hipStream_t stream, size_t bytes, float** ws) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.bytes < bytes) {
+        if (w.ws) (void)hipFree(w.ws);
+        w.ws = nullptr;
+        w.bytes = 0;
+        if ((e = hipMalloc(&w.ws, bytes)) != hipSuccess) return e;
+        w.bytes = bytes;
+    }
+    *ws = w.ws;
+    return hipSuccess;
+}
+
+int cu_count() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+            cus = n;
+        else
+            return 256;
+    }
+    return cus;
+}
+
+}  // namespace
 
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
@@ -422,10 +577,23 @@ hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, cons
     }
     const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
-    const int64_t chunk = (tiles + 7) / 8;
-    hipLaunchKernelGGL(gemm_slot2_kernel, dim3(unsigned(8 * chunk)), dim3(kThreads), size_t(kLds),
-                       stream, packed, scales, x, m, n, k, y, y_f16, int(tiles_n), int(tiles),
-                       int(chunk));
+    const Plan pl = plan_split(tiles, int(k / 512), cu_count());
+    const int64_t items = (tiles - pl.t0) * pl.splits;
+    float* ws = nullptr;
+    if (pl.splits > 1) {
+        const hipError_t e = get_workspace(stream, size_t(items) * kTileFloats * sizeof(float), &ws);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t chunk_a = (pl.t0 + 7) / 8, chunk_b = (items + 7) / 8;
+    hipLaunchKernelGGL(gemm_slot2_kernel, dim3(unsigned(8 * (chunk_a + chunk_b))), dim3(kThreads),
+                       size_t(kLds), stream, packed, scales, x, m, n, k, y, y_f16, int(tiles_n),
+                       int(tiles), pl.t0, int(chunk_a), pl.splits, int(chunk_b), ws);
+    if (pl.splits > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(256 * (tiles - pl.t0))), dim3(kThreads), 0, stream,
+                           ws, m, n, y, y_f16, int(tiles_n), pl.t0, pl.splits);
+    }
     return hipGetLastError();
 }
 
