@@ -25,7 +25,8 @@
  *     call returns TL_OK without synchronising.  A launch failure returns
  *     TL_ERR_LAUNCH and tl_last_error() gives the HIP error text (per thread).
  *   - The library keeps no state between calls apart from that per-thread
- *     error text; calls from several threads are safe.
+ *     error text and the K-split workspace of tl_gemm (below); calls from
+ *     several threads are safe.
  *
  * Formats (bit-exact; defined here, since the pages give no byte layout)
  *   digit d = code + 1, in {0, 1, 2}.
@@ -123,7 +124,15 @@ TL_API tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t 
  * weight tiles are expanded to exact binary16 (code * scale) on chip and fed
  * to fp16 matrix-core instructions with fp32 accumulation.  Prompt processing
  * is where the pages place the practical bottleneck on slower chips (Persian
- * page, paragraph 4). */
+ * page, paragraph 4).
+ * With TL_FMT_SLOT2, output tiles that would leave most of the GPU idle in a
+ * last partial round are split along K; their fp32 partial sums go to a
+ * workspace the library owns, one per (device, stream), and a second kernel
+ * adds them in a fixed order (results do not depend on scheduling).  The
+ * workspace is allocated with hipMalloc the first time a call needs it or
+ * more of it (so such a call cannot be captured into a HIP graph; later
+ * calls of equal or smaller shape allocate nothing) and is never freed before
+ * the process ends.  At most 16 parts x tiles of 256 x 256 fp32. */
 TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
                   void* y, int32_t y_dtype, hipStream_t stream);
