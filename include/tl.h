@@ -132,7 +132,10 @@ TL_API tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t 
  * workspace is allocated with hipMalloc the first time a call needs it or
  * more of it (so such a call cannot be captured into a HIP graph; later
  * calls of equal or smaller shape allocate nothing) and is never freed before
- * the process ends.  At most 16 parts x tiles of 256 x 256 fp32. */
+ * the process ends (under 1 GiB: at most 16 parts of 256 KB for each of
+ * fewer tiles than the GPU has compute units).  With TL_FMT_TRIT5 the
+ * weights are first rewritten as 2-bit slots (same codes; N * K/4 bytes) into
+ * a second such workspace, then multiplied the same way. */
 TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
                   void* y, int32_t y_dtype, hipStream_t stream);

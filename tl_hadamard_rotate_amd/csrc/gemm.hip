@@ -379,6 +379,16 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, c
     if (m < 1 || n < 1 || k < 1024 || k % 1024 != 0) return hipErrorInvalidValue;   // see the loop
     if (fmt == 1 && gemm_slot2_fits(m, n, k))
         return launch_gemm_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
+    if (fmt == 0 && gemm_slot2_fits(m, n, k)) {
+        // dense trits: rewritten as 2-bit slots once per call (one pass over
+        // the weights, small next to the product) for the same GEMM
+        void* slot2 = nullptr;
+        hipError_t e = workspace(kWorkspaceSlot2, stream, size_t(n) * size_t(k / 4), &slot2);
+        if (e != hipSuccess) return e;
+        if ((e = launch_trit5_to_slot2(packed, n, k, static_cast<uint8_t*>(slot2), stream)) != hipSuccess)
+            return e;
+        return launch_gemm_slot2(static_cast<const uint8_t*>(slot2), scales, x, m, n, k, y, y_f16, stream);
+    }
     return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
                     : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
 }

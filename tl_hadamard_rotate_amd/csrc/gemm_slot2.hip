@@ -41,10 +41,7 @@
 // workgroups of an XCD share activation rows in that XCD's L2.
 #include <hip/hip_fp16.h>
 
-#include <map>
-#include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "tl_internal.h"
 
@@ -522,33 +519,6 @@ Plan plan_split(int64_t tiles, int units, int cus) {
     return best;
 }
 
-// Partial-sum workspace, one per (device, stream), so that launches that may
-// overlap never share one; grown on demand (hipMalloc: such a call cannot be
-// captured into a graph), never shrunk.
-struct Workspace {
-    float* ws = nullptr;
-    size_t bytes = 0;
-};
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
-
-hipError_t get_workspace(hipStream_t stream, size_t bytes, float** ws) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    std::lock_guard<std::mutex> lock(g_ws_mutex);
-    Workspace& w = g_ws[{dev, stream}];
-    if (w.bytes < bytes) {
-        if (w.ws) (void)hipFree(w.ws);
-        w.ws = nullptr;
-        w.bytes = 0;
-        if ((e = hipMalloc(&w.ws, bytes)) != hipSuccess) return e;
-        w.bytes = bytes;
-    }
-    *ws = w.ws;
-    return hipSuccess;
-}
-
 int cu_count() {
     static int cus = 0;
     if (cus == 0) {
@@ -581,8 +551,10 @@ hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, cons
     const int64_t items = (tiles - pl.t0) * pl.splits;
     float* ws = nullptr;
     if (pl.splits > 1) {
-        const hipError_t e = get_workspace(stream, size_t(items) * kTileFloats * sizeof(float), &ws);
+        void* p = nullptr;
+        const hipError_t e = workspace(kWorkspacePartials, stream, size_t(items) * kTileFloats * sizeof(float), &p);
         if (e != hipSuccess) return e;
+        ws = static_cast<float*>(p);
     }
     const int64_t chunk_a = (pl.t0 + 7) / 8, chunk_b = (items + 7) / 8;
     hipLaunchKernelGGL(gemm_slot2_kernel, dim3(unsigned(8 * (chunk_a + chunk_b))), dim3(kThreads),

@@ -103,6 +103,50 @@ __global__ __launch_bounds__(kThreads) void unpack_slot2_kernel(
     }
 }
 
+// One thread per 128-code group: the dense trit packing rewritten as 2-bit
+// slots (32 bytes per group).  Bytes above 242, which the packer never
+// writes, decode as their base-3 digits, as in unpack_trit5_kernel.  The 26
+// bytes are read as the 7 dwords from the one holding the group's first byte
+// (in bounds for every group: the last group of a row starts at 2 mod 4).
+template <int O>
+__device__ __forceinline__ void trit5_group_to_slot2(const uint32_t (&dw)[7], uint32_t (&w)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 26; ++j) {
+        uint32_t v = (dw[(O + j) >> 2] >> (8 * ((O + j) & 3))) & 0xFFu;
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            const int c = 5 * j + i;
+            const uint32_t q = (v * 171u) >> 9;   // v / 3 for v < 256
+            if (c < kGroup) w[c >> 4] |= (v - 3u * q) << (2 * (c & 15));
+            v = q;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void trit5_to_slot2_kernel(
+    const uint8_t* __restrict__ trit5, int64_t n, int64_t k, uint8_t* __restrict__ slot2) {
+    const int64_t groups = k / kGroup;
+    const int64_t total = n * groups;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const int64_t row = idx / groups, g = idx - row * groups;
+        const int64_t start = row * groups * kTrit5GroupBytes + g * kTrit5GroupBytes;
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(trit5 + (start & ~int64_t(3)));
+        uint32_t dw[7], w[8];
+#pragma unroll
+        for (int i = 0; i < 7; ++i) dw[i] = src[i];
+        if (start & 3)
+            trit5_group_to_slot2<2>(dw, w);
+        else
+            trit5_group_to_slot2<0>(dw, w);
+        uint4* dst = reinterpret_cast<uint4*>(slot2 + row * (k / 4) + g * 32);
+        dst[0] = uint4{w[0], w[1], w[2], w[3]};
+        dst[1] = uint4{w[4], w[5], w[6], w[7]};
+    }
+}
+
 unsigned grid_for(int64_t total) {
     int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
@@ -123,6 +167,13 @@ hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt, uint8
         hipLaunchKernelGGL(pack_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
                            codes, n, k, packed, bad_count);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uint8_t* slot2,
+                                 hipStream_t stream) {
+    hipLaunchKernelGGL(trit5_to_slot2_kernel, dim3(grid_for(n * (k / kGroup))), dim3(kThreads), 0,
+                       stream, trit5, n, k, slot2);
     return hipGetLastError();
 }
 

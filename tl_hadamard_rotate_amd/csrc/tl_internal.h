@@ -37,6 +37,14 @@ hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales,
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
+// Library-owned device workspace of `kind` for `stream` on the current
+// device, at least `bytes` long (grown with hipMalloc when needed).
+enum { kWorkspacePartials = 0, kWorkspaceSlot2 = 1 };
+hipError_t workspace(int kind, hipStream_t stream, size_t bytes, void** out);
+// The dense trit packing rewritten as 2-bit slots (same codes), row-major
+// [n][k/4] bytes.
+hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uint8_t* slot2,
+                                 hipStream_t stream);
 // Prefill GEMM of the 2-bit-slot packing with the weights decoded in
 // registers; usable when gemm_slot2_fits(m, n, k)
 bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
