@@ -356,6 +356,42 @@ def profile_pass(torch, tl, synth, dev, fmt) -> int:
     return 0
 
 
+def profile_prefill(torch, tl, synth, dev) -> int:
+    """Kernels for the prefill counter runs: the calibration copy (3 launches
+    of a 256 MiB device copy), then 3 launches each of the 2-bit-slot GEMM at
+    M=4096 for gate (K=5120, N=17408) and down (K=17408, N=5120), then 3
+    launches each of the rotation at M=4096 for K=5120 and K=17408."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for name in ("gate", "down"):
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=synth.LINEAR_ID[name])
+        packed = tl.pack(torch.from_numpy(inp.codes).to(dev), 1)
+        scales = torch.from_numpy(inp.scales).to(dev)
+        gen = torch.Generator(device="cpu").manual_seed(4 + 4096)
+        x = torch.randn((4096, k), generator=gen).to(torch.float16).to(dev)
+        y = torch.empty((4096, n), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            tl.gemm(packed, scales, 1, x, out=y)
+        torch.cuda.synchronize()
+        del packed, scales, x, y
+    for k in (5120, 17408):
+        gen = torch.Generator(device="cpu").manual_seed(k)
+        x = torch.randn((4096, k), generator=gen).to(torch.float16).to(dev)
+        s = (torch.randint(0, 2, (k,), generator=gen) * 2 - 1).to(torch.int8).to(dev)
+        o = torch.empty_like(x)
+        for _ in range(3):
+            tl.hadamard_rotate(x, s, out=o)
+        torch.cuda.synchronize()
+        del x, s, o
+    log("prefill profile pass done")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,6 +405,9 @@ def main(argv=None) -> int:
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs under rocprofv3: a 256 MiB device copy (the calibration "
                          "kernel, 3 launches) then 10 eager passes of the step's GEMVs; no timing")
+    ap.add_argument("--profile-prefill", action="store_true",
+                    help="for counter runs under rocprofv3: the calibration copy, then the prefill "
+                         "GEMM (M=4096, gate and down) and the rotation at M=4096; no timing")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -386,6 +425,8 @@ def main(argv=None) -> int:
     stream = torch.cuda.Stream(dev)
     if args.profile_pass:
         return profile_pass(torch, tl, synth, dev, fmt)
+    if args.profile_prefill:
+        return profile_prefill(torch, tl, synth, dev)
     log(f"building inputs fmt={args.fmt} copies={args.copies}")
     lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
     with torch.cuda.stream(stream):
