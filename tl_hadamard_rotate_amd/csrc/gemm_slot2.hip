@@ -8,12 +8,12 @@
 // LDS.  Prompt processing is the bottleneck the pages name for slower chips
 // (page "A 27-billion model that fits in 8.6 GB", paragraph 4).
 //
-// Tiling: a workgroup of 4 waves (one per SIMD, each with the whole register
-// file: 256 accumulators in AGPRs) computes a 256 x 256 output tile (M x N);
-// wave w owns the 128 x 128 sub-tile (w / 2, w % 2): 4 x 4 MFMA tiles of
-// 32 x 32.  Per K step (64) a wave issues 64 MFMAs and reads 16 KB of
-// activations from LDS: 12 KB of LDS traffic per MFLOP, against 50 KB for
-// 64 x 64 sub-tiles with the weights staged in LDS as well.
+// Tiling: a workgroup of 8 waves (two per SIMD) computes a 256 x 256 output
+// tile (M x N); wave w owns the 128 x 64 sub-tile (w / 4, w % 4): 4 x 2 MFMA
+// tiles of 32 x 32, 128 fp32 accumulators per lane.  Per K step (64) a wave
+// issues 32 MFMAs, decodes 64 weights per lane and reads 16 KB of activations
+// from LDS: 16 KB of LDS traffic per MFLOP, against 50 KB for 64 x 64
+// sub-tiles with the weights staged in LDS as well.
 //
 // K order inside an MFMA is free as long as the A and B operands agree, and
 // it is chosen so that a lane's weights of a step are 8 contiguous packed
@@ -56,8 +56,17 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kWaves = 4;
+// 8 waves: two per SIMD, 128 x 64 sub-tiles, 128 accumulators (the other wave
+// of a SIMD issues while one waits; 8-18 % faster than 4 waves of 128 x 128
+// sub-tiles with the whole register file, measured over the MLP shapes)
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesN = kWaves / 2;          // waves along N (two along M)
+constexpr int NJ = 16 / kWaves;              // 32-wide MFMA column tiles per wave
+constexpr int kRegs = 4 * NJ * 16;           // accumulators per lane
+constexpr int kALoads = 32 / kWaves;         // 1 KB activation loads per wave per step
+constexpr int kBLoads = 16 / kWaves;         // 256 B weight loads per wave per step
+constexpr int kVmWait = kALoads + kBLoads;   // fewest loads a wave issues in a step
 constexpr int kAStage = BM * BK * 2;   // 32 KB
 constexpr int kStages = 4;
 constexpr int kTileFloats = BM * BN;   // partial sums of one tile
@@ -97,7 +106,7 @@ __device__ __forceinline__ void decode8(uint32_t w, int h, ScaleSel sc, uint32_t
     }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_slot2_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void gemm_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m, int64_t n,
     int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int t0, int chunk_a,
     int splits, int chunk_b, float* __restrict__ ws) {
@@ -138,7 +147,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     const uint32_t groups = uint32_t(k / kGroup);
     const uint32_t row_bytes = uint32_t(k / 4);
 
-    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128;
+    const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * NJ);
     const int q = lane >> 5;
 
     // LDS: four activation and four weight stages (one step each), two scale
@@ -150,14 +159,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // so the loop holds no register loads and the only waits on memory are
     // the explicit ones before each barrier.
     //
-    // Activations, 1 KB per load: wave w stages tile rows 64 w .. 64 w + 63,
-    // eight rows per load; load u puts row 64 w + 8 u + i / 8, physical chunk
-    // i % 8, which holds logical chunk (i % 8) ^ ((row >> 1) & 7), i.e.
-    // ((i % 8) ^ (i / 16 + 4 (u % 2))).
-    uint32_t aoff[8];   // byte offsets
+    // Activations, 1 KB per load: wave w stages tile rows 32 w .. 32 w + 31,
+    // eight rows per load (four loads); load u puts row 32 w + 8 u + i / 8,
+    // physical chunk i % 8, which holds logical chunk (i % 8) ^ ((row >> 1) &
+    // 7), i.e. ((i % 8) ^ (i / 16 + 4 (u % 2))).
+    uint32_t aoff[kALoads];   // byte offsets
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        const int64_t r = m0 + 64 * wave + 8 * u + (lane >> 3);
+    for (int u = 0; u < kALoads; ++u) {
+        const int64_t r = m0 + (256 / kWaves) * wave + 8 * u + (lane >> 3);
         const uint32_t gm = uint32_t(r < m ? r : m - 1);   // rows past M copy row M-1
         const uint32_t c = uint32_t((lane & 7) ^ ((lane >> 4) + 4 * (u & 1)));
         aoff[u] = 2u * (gm * uint32_t(k) + 128u * (c >> 2) + 8u * (c & 3u));
@@ -167,19 +176,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const uint32_t o = 512u * uint32_t(t >> 2) + 64u * uint32_t(t & 3);
         __builtin_amdgcn_global_load_lds(
             (__attribute__((address_space(1))) void*)(uintptr_t)(xb + (aoff[u] + o)),
-            (__attribute__((address_space(3))) void*)(uintptr_t)(stage + 8192u * uint32_t(wave) + 1024u * u),
+            (__attribute__((address_space(3))) void*)(uintptr_t)(stage + (32768u / kWaves) * uint32_t(wave) + 1024u * u),
             16, 0, 0);
     };
     // Packed weights, 4 bytes per lane and load: the weight stage of step t
     // (step t % 4 of block T = t / 4) holds, per tile row n and K half h, the
     // 8 bytes (32 codes) at byte 64 T + 32 h + 8 (t % 4) of the row:
-    // [n][h][8 B].  Wave w loads rows 64 w .. 64 w + 63, 16 rows per 256-byte
-    // load: lane i of load v takes row 64 w + 16 v + i / 4, half (i / 2) % 2,
-    // dword i % 2.
-    uint32_t boff[4];
+    // [n][h][8 B].  Wave w loads rows 32 w .. 32 w + 31, 16 rows per 256-byte
+    // load (two loads): lane i of load v takes row 32 w + 16 v + i / 4, half
+    // (i / 2) % 2, dword i % 2.
+    uint32_t boff[kBLoads];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int64_t r = n0 + 64 * wave + 16 * v + (lane >> 2);
+    for (int v = 0; v < kBLoads; ++v) {
+        const int64_t r = n0 + (256 / kWaves) * wave + 16 * v + (lane >> 2);
         const uint32_t gn = uint32_t(r < n ? r : n - 1);   // rows past N decode row N-1
         boff[v] = gn * row_bytes + 32u * uint32_t((lane >> 1) & 1) + 4u * uint32_t(lane & 1);
     }
@@ -187,19 +196,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         const uint32_t o = 64u * uint32_t(t >> 2) + 8u * uint32_t(t & 3);
         __builtin_amdgcn_global_load_lds(
             (__attribute__((address_space(1))) void*)(uintptr_t)(packed + (boff[v] + o)),
-            (__attribute__((address_space(3))) void*)(uintptr_t)(stage + 1024u * uint32_t(wave) + 256u * v),
+            (__attribute__((address_space(3))) void*)(uintptr_t)(stage + (4096u / kWaves) * uint32_t(wave) + 256u * v),
             4, 0, 0);
     };
     // Scales, per block: the scale stage holds the dword of groups
-    // (2T, 2T + 1) of each tile row, [n][4 B]; wave w loads rows 64 w .. +63.
+    // (2T, 2T + 1) of each tile row, [n][4 B]; waves 0..3 load rows 64 w .. +63.
     uint32_t soff;
     {
-        const int64_t r = n0 + 64 * wave + lane;
+        const int64_t r = n0 + 64 * (wave & 3) + lane;
         const uint32_t gn = uint32_t(r < n ? r : n - 1);
         soff = 2u * gn * groups;
     }
     const char* sb = reinterpret_cast<const char*>(scales);
-    auto dma_s = [&](uint32_t stage, int t_blk) {
+    auto dma_s = [&](uint32_t stage, int t_blk) {   // waves 0..3, 64 rows each
+        if (wave >= 4) return;
         __builtin_amdgcn_global_load_lds(
             (__attribute__((address_space(1))) void*)(uintptr_t)(sb + (soff + 4u * uint32_t(t_blk))),
             (__attribute__((address_space(3))) void*)(uintptr_t)(stage + 256u * uint32_t(wave)), 4, 0, 0);
@@ -214,11 +224,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // Pipeline.  During step t the MFMAs read step t's activation stage; the
     // fragments and weights of the next K slice are read from LDS (and the
     // weights decoded) while a slice's MFMAs run, step t + 1's first slice
-    // during step t's last.  Step t loads, a quarter per K slice, step t + 3's
-    // activations and weights into the stages step t - 1 used and, in a
-    // block's first step, the next block's scales.  At the end of step t,
-    // s_waitcnt vmcnt(8) leaves at most the wave's 8 newest loads outstanding;
-    // every step issues at least 12, so every load of step t - 1 is complete,
+    // during step t's last.  Step t loads, spread over its K slices, step
+    // t + 3's activations and weights into the stages step t - 1 used and, in
+    // a block's first step, the next block's scales.  At the end of step t,
+    // s_waitcnt vmcnt(6) leaves at most the wave's 6 newest loads outstanding;
+    // every step issues at least 6, so every load of step t - 1 is complete,
     // and after the barrier all that step t + 1 reads is in LDS: activations
     // and weights of step t + 2 and scales of the block of t + 2.  Stage
     // reuse: the stages step t + 3 takes were last read in step t - 1 (its
@@ -241,9 +251,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < 3; ++i) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) dma_a(stg_a[i], tb + i, u);
+        for (int u = 0; u < kALoads; ++u) dma_a(stg_a[i], tb + i, u);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dma_b(stg_b[i], tb + i, v);
+        for (int v = 0; v < kBLoads; ++v) dma_b(stg_b[i], tb + i, v);
     }
     dma_s(stg_s[0], tb >> 2);
     __builtin_amdgcn_sched_barrier(0);
@@ -257,14 +267,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                 half8, *reinterpret_cast<lds_u32x4*>(base + swz(wm + 32 * i + (lane & 31), 4 * q + s)));
     };
     // this lane's 8 bytes of a step for rows j
-    auto read_b = [&](uint2 (&w)[4], uint32_t stage) {
+    auto read_b = [&](uint2 (&w)[NJ], uint32_t stage) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             w[j] = __builtin_bit_cast(uint2, *reinterpret_cast<lds_u32x2*>(stage + (brow + 32u * j) * 16u + 8u * q));
     };
-    auto read_sc = [&](ScaleSel (&sc)[4], uint32_t stage) {
+    auto read_sc = [&](ScaleSel (&sc)[NJ], uint32_t stage) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
             sc[j] = scale_sel(*reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(
                 stage + (brow + 32u * j) * 4u + 2u * q));
     };
@@ -272,44 +282,58 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     // cannot tell them from reads of a stage a load is filling and makes
     // them wait for every load in flight.  Each block waits for its own
     // reads (and the LDS reads before them) before it ends.
-    auto read_b_asm = [&](uint2 (&w)[4], uint32_t stage) {
+    auto read_b_asm = [&](uint2 (&w)[NJ], uint32_t stage) {
         const uint32_t a = stage + brow * 16u + 8u * q;
-        uint64_t r0, r1, r2, r3;
-        asm volatile(
-            "ds_read_b64 %0, %4\n\t"
-            "ds_read_b64 %1, %4 offset:512\n\t"
-            "ds_read_b64 %2, %4 offset:1024\n\t"
-            "ds_read_b64 %3, %4 offset:1536\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-            : "v"(a)
-            : "memory");
-        w[0] = __builtin_bit_cast(uint2, r0);
-        w[1] = __builtin_bit_cast(uint2, r1);
-        w[2] = __builtin_bit_cast(uint2, r2);
-        w[3] = __builtin_bit_cast(uint2, r3);
+        uint64_t r[4];
+        if (NJ == 4)
+            asm volatile(
+                "ds_read_b64 %0, %4\n\t"
+                "ds_read_b64 %1, %4 offset:512\n\t"
+                "ds_read_b64 %2, %4 offset:1024\n\t"
+                "ds_read_b64 %3, %4 offset:1536\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                : "v"(a)
+                : "memory");
+        else
+            asm volatile(
+                "ds_read_b64 %0, %2\n\t"
+                "ds_read_b64 %1, %2 offset:512\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1])
+                : "v"(a)
+                : "memory");
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) w[j] = __builtin_bit_cast(uint2, r[j]);
     };
-    auto read_sc_asm = [&](ScaleSel (&sc)[4], uint32_t stage) {
+    auto read_sc_asm = [&](ScaleSel (&sc)[NJ], uint32_t stage) {
         const uint32_t a = stage + brow * 4u + 2u * q;
-        uint32_t r0, r1, r2, r3;
-        asm volatile(
-            "ds_read_u16 %0, %4\n\t"
-            "ds_read_u16 %1, %4 offset:128\n\t"
-            "ds_read_u16 %2, %4 offset:256\n\t"
-            "ds_read_u16 %3, %4 offset:384\n\t"
-            "s_waitcnt lgkmcnt(0)"
-            : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-            : "v"(a)
-            : "memory");
-        sc[0] = scale_sel(r0);
-        sc[1] = scale_sel(r1);
-        sc[2] = scale_sel(r2);
-        sc[3] = scale_sel(r3);
+        uint32_t r[4];
+        if (NJ == 4)
+            asm volatile(
+                "ds_read_u16 %0, %4\n\t"
+                "ds_read_u16 %1, %4 offset:128\n\t"
+                "ds_read_u16 %2, %4 offset:256\n\t"
+                "ds_read_u16 %3, %4 offset:384\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+                : "v"(a)
+                : "memory");
+        else
+            asm volatile(
+                "ds_read_u16 %0, %2\n\t"
+                "ds_read_u16 %1, %2 offset:128\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(r[0]), "=&v"(r[1])
+                : "v"(a)
+                : "memory");
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sc[j] = scale_sel(r[j]);
     };
     // B operands of slice s (codes 8s .. 8s + 7 of the step's 32 per row)
-    auto decode_bf = [&](half8 (&bf)[4], const uint2 (&w)[4], const ScaleSel (&sc)[4], int s) {
+    auto decode_bf = [&](half8 (&bf)[NJ], const uint2 (&w)[NJ], const ScaleSel (&sc)[NJ], int s) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NJ; ++j) {
             uint32_t o[4];
             decode8(s < 2 ? w[j].x : w[j].y, s & 1, sc[j], mask, bits, o);
             bf[j] = __builtin_bit_cast(half8, u32x4{o[0], o[1], o[2], o[3]});
@@ -317,19 +341,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     };
 
     // operands of slice s sit in buffer s % 2; weights of step t in rb[t % 2]
-    half8 af[2][4], bf[2][4];
-    uint2 rb[2][4];
-    ScaleSel sc[2][4];   // blocks T and T + 1
+    half8 af[2][4], bf[2][NJ];
+    uint2 rb[2][NJ];
+    ScaleSel sc[2][NJ];   // blocks T and T + 1
     read_sc(sc[0], stg_s[0]);
     read_b(rb[0], stg_b[0]);
     read_af(af[0], stg_a[0], 0);
     decode_bf(bf[0], rb[0], sc[0], 0);
 
-    float16v acc[4][4];
+    float16v acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
@@ -345,9 +369,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             // loads, pinned at the slice start: the compiler makes a load into
             // LDS wait for every LDS read in flight, here only the previous
             // slice's, which this slice's MFMAs need anyway
-            dma_a(stg_a[3], t3, 2 * s);
-            dma_a(stg_a[3], t3, 2 * s + 1);
-            dma_b(stg_b[3], t3, s);
+#pragma unroll
+            for (int u = s * kALoads / 4; u < (s + 1) * kALoads / 4; ++u) dma_a(stg_a[3], t3, u);
+            if (kBLoads == 4 || !(s & 1)) dma_b(stg_b[3], t3, kBLoads == 4 ? s : s >> 1);
             if (s == 2 && TT == 0) dma_s(stg_s[1], b1);
             __builtin_amdgcn_sched_barrier(0);
             if (s < 3) {
@@ -364,25 +388,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < NJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[s & 1][i], bf[s & 1][j], acc[i][j],
                                                                        0, 0, 0);
-#ifdef TL_GEMM_SCHED
-            // next slice's LDS reads first, then each MFMA followed by a few
-            // VALU operations of the next slice's decode
-            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, TL_GEMM_SCHED, 0);
-            }
-#endif
-#ifdef TL_GEMM_KEEP
-            // this slice's operands stay allocated to the end of the slice, so
-            // the next decode never writes a register an MFMA in flight reads
-            asm volatile("" ::"v"(af[s & 1][0]), "v"(af[s & 1][1]), "v"(af[s & 1][2]), "v"(af[s & 1][3]),
-                         "v"(bf[s & 1][0]), "v"(bf[s & 1][1]), "v"(bf[s & 1][2]), "v"(bf[s & 1][3]));
-#endif
         }
         {   // rotate the stages
             const uint32_t a0 = stg_a[0];
@@ -400,7 +408,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" : : : "memory");
+        static_assert(kVmWait == 6, "the wait below counts the loads of a step");
+        asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" : : : "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
     using C0 = std::integral_constant<int, 0>;
@@ -430,9 +439,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mine[((i * 4 + j) * 16 + r) * kThreads + tid] = acc[i][j][r];
+                for (int r = 0; r < 16; ++r) mine[((i * NJ + j) * 16 + r) * kThreads + tid] = acc[i][j][r];
         return;
     }
 
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
@@ -464,16 +473,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 __global__ __launch_bounds__(kThreads) void gemm_slot2_reduce(const float* __restrict__ ws,
                                                               int64_t m, int64_t n, void* __restrict__ y,
                                                               int y_f16, int tiles_n, int t0, int splits) {
-    const int tt = int(blockIdx.x >> 8), e = int(blockIdx.x & 255);
+    const int tt = int(blockIdx.x) / kRegs, e = int(blockIdx.x) % kRegs;
     const int tile = t0 + tt;
     const int64_t m0 = int64_t(tile / tiles_n) * BM;
     const int64_t n0 = int64_t(tile % tiles_n) * BN;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = (wave >> 1) * 128, wn = (wave & 1) * 128, q = lane >> 5;
+    const int wm = (wave / kWavesN) * 128, wn = (wave % kWavesN) * (32 * NJ), q = lane >> 5;
     const float* parts = ws + size_t(tt) * splits * kTileFloats + e * kThreads + tid;
     float sum = parts[0];
     for (int p = 1; p < splits; ++p) sum += parts[size_t(p) * kTileFloats];
-    const int i = e >> 6, j = (e >> 4) & 3, r = e & 15;
+    const int i = e / (16 * NJ), j = (e / 16) % NJ, r = e % 16;
     const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
     const int64_t col = n0 + wn + 32 * j + (lane & 31);
     if (row < m && col < n) {
@@ -563,7 +572,7 @@ hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, cons
     if (pl.splits > 1) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(256 * (tiles - pl.t0))), dim3(kThreads), 0, stream,
+        hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(kRegs * (tiles - pl.t0))), dim3(kThreads), 0, stream,
                            ws, m, n, y, y_f16, int(tiles_n), pl.t0, pl.splits);
     }
     return hipGetLastError();
