@@ -22,7 +22,8 @@ is the one those counters were taken from.
 
 Extras: the other packing, the prefill GEMM sweep, batched decode over the
 attention projections, the rotation at prefill size, the 64-layer weight
-stream, and the CPU oracle on a bounded sample.
+stream (one rotation per linear, and one per input with q|k|v and gate|up
+concatenated), and the CPU oracle on a bounded sample.
 
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
@@ -335,6 +336,65 @@ def bench_stream(torch, tl, synth, dev, fmt, stream, reps=5):
             "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
 
 
+def bench_stream_shared(torch, tl, synth, dev, fmt, stream, reps=5):
+    """The same 64-layer weight stream with one rotation per input instead of
+    one per linear: q, k, v (which read the same input) concatenated along N
+    into one linear, and gate, up likewise; 4 tl_linear calls per layer
+    instead of 7.  Same weight bytes."""
+    import numpy as np
+
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    layer = []
+    for grp in groups:
+        k = synth.SHAPES[grp[0]][0]
+        ins = [synth.linear_inputs(synth.SHAPES[g][1], k, 1, seed=0, cfg=5, layer=0,
+                                   linear=synth.LINEAR_ID[g], outliers=g in ("q", "k", "v", "o"))
+               for g in grp]
+        codes = torch.from_numpy(np.concatenate([i.codes for i in ins])).to(dev)
+        scales = torch.from_numpy(np.concatenate([i.scales for i in ins])).to(dev)
+        layer.append((k, codes.shape[0], tl.pack(codes, fmt), scales,
+                      torch.from_numpy(ins[0].signs).to(dev), torch.from_numpy(ins[0].x).to(dev)))
+        del codes
+    lins = []
+    for li in range(synth.N_LAYERS):
+        for k, n, p, sc, sg, x in layer:
+            lins.append(dict(k=k, n=n, packed=p if li == 0 else p.clone(),
+                             scales=sc if li == 0 else sc.clone(), signs=sg, x=x,
+                             x_rot=torch.empty((1, k), dtype=torch.float16, device=dev),
+                             y=torch.empty((1, n), dtype=torch.float32, device=dev)))
+    weight_bytes = sum(l["packed"].numel() + l["scales"].numel() * 2 for l in lins)
+    act_bytes = sum(rotate_bytes(1, l["k"]) + 2 * l["k"] + 4 * l["n"] for l in lins)
+
+    def token():
+        for l in lins:
+            tl.linear(l["packed"], l["scales"], fmt, l["x"], l["signs"], out=l["y"],
+                      x_rot=l["x_rot"])
+
+    with torch.cuda.stream(stream):
+        token()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            token()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del g, lins, layer
+    torch.cuda.empty_cache()
+    return {"layers": synth.N_LAYERS, "linear_calls_per_layer": len(groups),
+            "linear_calls_per_token": synth.N_LAYERS * len(groups),
+            "weight_bytes": int(weight_bytes), "activation_bytes": int(act_bytes),
+            "ms_per_token": round(ms, 4), "weight_streams_per_s": round(1e3 / ms, 1),
+            "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
+
+
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
     256 MiB written per launch), then 10 eager decode steps (per projection
@@ -491,6 +551,9 @@ def main(argv=None) -> int:
         extra["rotate_prefill"] = bench_rotate_prefill(torch, tl, dev)
         log("64-layer weight stream")
         extra["weight_stream"] = bench_stream(torch, tl, synth, dev, fmt, stream)
+        log("64-layer weight stream, one rotation per input (q|k|v and gate|up concatenated)")
+        extra["weight_stream_shared_rotation"] = bench_stream_shared(torch, tl, synth, dev, fmt,
+                                                                     stream)
 
     cpu = None
     if not args.no_cpu_baseline:

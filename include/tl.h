@@ -153,7 +153,11 @@ TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t 
  * TL_FMT_SLOT2 (and K <= 20480) the rotation runs inside the GEMV kernel: one
  * launch, the rotated activations never make a round trip through memory
  * before use (x_rot is still written).  Otherwise: tl_hadamard_rotate, then
- * tl_gemv (M < 64) or tl_gemm (M >= 64). */
+ * tl_gemv (M < 64) or tl_gemm (M >= 64).
+ * Linears that read the same input (q, k, v; gate, up) share its rotation:
+ * the signs belong to the input, so their packed rows and scales can be
+ * concatenated along N (row-major, so plain concatenation) and run as one
+ * call, which rotates once and launches once. */
 TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                     const uint16_t* x, const int8_t* signs, int64_t M, int64_t N, int64_t K,
                     uint16_t* x_rot, void* y, int32_t y_dtype, hipStream_t stream);

@@ -332,3 +332,36 @@ def test_linear_full_size_sampled_rows(gpu, shape):
     rows = np.concatenate([np.random.default_rng(1).choice(n, size=200, replace=False), [0, n - 1]])
     want = oracle.linear(inp.x, inp.signs, inp.codes[rows], inp.scales[rows])[0]
     assert oracle.rel_l2(y[rows], want) < 2e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("gate", "up")])
+def test_linear_shared_rotation_concatenated(gpu, fmt, group):
+    """Linears that read the same input share one rotation: their packed rows
+    and scales concatenated along N go through one tl_linear call.  Each row's
+    result is the one its own call gives: bit for bit with 2-bit slots (the
+    fused kernel adds a row's parts in an order that does not depend on the
+    other rows), to fp32 rounding with dense trits (that GEMV splits K across
+    waves by the size of a CU's slice of rows, which depends on N); sampled
+    rows match the oracle's layer."""
+    k = synth.SHAPES[group[0]][0]
+    parts = [synth.linear_inputs(synth.SHAPES[g][1], k, 1, cfg=5, linear=synth.LINEAR_ID[g],
+                                 outliers=g in ("q", "k", "v")) for g in group]
+    x, signs = parts[0].x, parts[0].signs     # the shared input and its rotation
+    codes = np.concatenate([p.codes for p in parts])
+    scales = np.concatenate([p.scales for p in parts])
+    xd, sd = dev(x, gpu), dev(signs, gpu)
+    y_all = host(tl.linear(tl.pack(dev(codes, gpu), fmt), dev(scales, gpu), fmt, xd, sd))[0]
+    off = 0
+    for p in parts:
+        n = p.codes.shape[0]
+        y_one = host(tl.linear(tl.pack(dev(p.codes, gpu), fmt), dev(p.scales, gpu), fmt, xd, sd))[0]
+        if fmt == tl.FMT_SLOT2:
+            assert np.array_equal(y_all[off:off + n].view(np.uint32), y_one.view(np.uint32))
+        else:
+            assert np.allclose(y_all[off:off + n], y_one, rtol=1e-5, atol=1e-6 * np.abs(y_one).max())
+        off += n
+    n = codes.shape[0]
+    rows = np.concatenate([np.random.default_rng(2).choice(n, size=160, replace=False), [0, n - 1]])
+    want = oracle.linear(x, signs, codes[rows], scales[rows])[0]
+    assert oracle.rel_l2(y_all.astype(np.float64)[rows], want) < 2e-3
