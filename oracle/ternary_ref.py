@@ -20,6 +20,9 @@ What it computes (every step is the plain definition, no fast algorithm):
   section "How it works", step 1 (the rotation is signed).
 * Two byte packings of the same codes: a dense one with 5 trits per byte and
   one with a 2-bit slot per value.  Source: the Persian page, paragraph 5.
+* A binary variant: every weight is -1 or +1 with one scale per 128 weights,
+  about 1.125 bits per weight.  Source: page "How Prism ML Squeezed a 27B
+  Model Into 3.9 GB" (dev.to), list "Two formats ship today".
 
 Readings taken where the pages are silent (all listed in the design doc):
 
@@ -29,7 +32,8 @@ Readings taken where the pages are silent (all listed in the design doc):
 * digit d = c + 1.  TRIT5: per 128-group 26 bytes; byte j < 25 holds digits
   5j..5j+4 little-endian in base 3; byte 25 holds digits 125..127 plus two
   pad digits equal to 1 (code 0).  SLOT2: byte j holds digits 4j..4j+3,
-  two bits each, least significant first.
+  two bits each, least significant first.  BIT1 (codes -1 and +1 only):
+  byte j holds bits b[8j..8j+7], least significant first, code = 2b - 1.
 * Scales: binary16 array [N, K/128]; a weight is c * S.
 
 Parity status of every function here is recorded in the design doc; the pins live
@@ -44,6 +48,7 @@ GROUP = 128           # weights per FP16 scale (Persian page, paragraph 2)
 
 FMT_TRIT5 = 0
 FMT_SLOT2 = 1
+FMT_BIT1 = 2
 
 TRIT5_GROUP_BYTES = 26   # 25 bytes of 5 trits + 1 byte of 3 trits and 2 pads
 _POW3 = (1, 3, 9, 27, 81)
@@ -123,6 +128,8 @@ def packed_bytes(n: int, k: int, fmt: int, group: int = GROUP) -> int:
         return n * (k // group) * trit5_group_bytes(group)
     if fmt == FMT_SLOT2:
         return n * k // 4
+    if fmt == FMT_BIT1:
+        return n * k // 8
     raise ValueError("unknown format")
 
 
@@ -189,11 +196,34 @@ def unpack_slot2(packed: np.ndarray, k: int) -> np.ndarray:
     return (d.reshape(p.shape[0], k) - 1).astype(np.int8)
 
 
+def pack_bit1(codes: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """codes [N, K] in {-1, +1} -> uint8 [N, K/8]; byte j bit i = b[8j+i],
+    b = (c + 1) / 2."""
+    c = _check_codes(codes, group)
+    if (c == 0).any():
+        raise ValueError("BIT1 codes must be -1 or +1")
+    n, k = c.shape
+    b = ((c + 1) // 2).reshape(n, k // 8, 8)
+    vals = (b << np.arange(8, dtype=np.int64)).sum(axis=-1)
+    return vals.astype(np.uint8)
+
+
+def unpack_bit1(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of ``pack_bit1``: every byte is valid."""
+    p = np.asarray(packed, dtype=np.int64)
+    if p.shape[1] * 8 != k:
+        raise ValueError("packed width does not match K")
+    b = (p[:, :, None] >> np.arange(8, dtype=np.int64)) & 1
+    return (2 * b.reshape(p.shape[0], k) - 1).astype(np.int8)
+
+
 def pack(codes: np.ndarray, fmt: int, group: int = GROUP) -> np.ndarray:
     if fmt == FMT_TRIT5:
         return pack_trit5(codes, group)
     if fmt == FMT_SLOT2:
         return pack_slot2(codes, group)
+    if fmt == FMT_BIT1:
+        return pack_bit1(codes, group)
     raise ValueError("unknown format")
 
 
@@ -202,6 +232,8 @@ def unpack(packed: np.ndarray, k: int, fmt: int, group: int = GROUP) -> np.ndarr
         return unpack_trit5(packed, k, group)
     if fmt == FMT_SLOT2:
         return unpack_slot2(packed, k)
+    if fmt == FMT_BIT1:
+        return unpack_bit1(packed, k)
     raise ValueError("unknown format")
 
 
@@ -231,6 +263,22 @@ def pack_slot2_loop(codes) -> bytes:
             val = 0
             for i in range(4):
                 val |= (row[j + i] + 1) << (2 * i)
+            out.append(val)
+    return bytes(out)
+
+
+def pack_bit1_loop(codes) -> bytes:
+    """Byte-by-byte pure-Python BIT1 packer for tiny inputs."""
+    out = bytearray()
+    for row in codes:
+        row = [int(v) for v in row]
+        for j in range(0, len(row), 8):
+            val = 0
+            for i in range(8):
+                if row[j + i] == 1:
+                    val |= 1 << i
+                elif row[j + i] != -1:
+                    raise ValueError("BIT1 codes must be -1 or +1")
             out.append(val)
     return bytes(out)
 

@@ -10,7 +10,7 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(ref, name) for name in
          ("hadamard", "rotate", "dequant", "matvec", "pack_trit5", "unpack_trit5",
-          "pack_slot2", "unpack_slot2")}
+          "pack_slot2", "unpack_slot2", "pack_bit1", "unpack_bit1")}
 
 
 def _rotate_signs_last(x, signs, block=ref.BLOCK):
@@ -86,6 +86,17 @@ def _pack_slot2_signed(codes, group=ref.GROUP):
     return (d << np.array([0, 2, 4, 6])).sum(-1).astype(np.uint8)
 
 
+def _pack_bit1_msb_first(codes, group=ref.GROUP):
+    c = np.asarray(codes, dtype=np.int64)
+    n, k = c.shape
+    b = ((c + 1) // 2).reshape(n, k // 8, 8)
+    return (b << np.arange(7, -1, -1)).sum(-1).astype(np.uint8)
+
+
+def _unpack_bit1_inverted(packed, k):
+    return (-_orig["unpack_bit1"](packed, k)).astype(np.int8)
+
+
 MUTATIONS = {
     "rotate: signs after H": ("rotate", _rotate_signs_last),
     "rotate: 1/n instead of 1/sqrt(n)": ("rotate", _rotate_wrong_norm),
@@ -96,6 +107,8 @@ MUTATIONS = {
     "matvec: transposed weight": ("matvec", _matvec_transposed),
     "pack_trit5: most significant trit first": ("pack_trit5", _pack_trit5_big_endian),
     "pack_slot2: two's complement slots": ("pack_slot2", _pack_slot2_signed),
+    "pack_bit1: most significant bit first": ("pack_bit1", _pack_bit1_msb_first),
+    "unpack_bit1: bit 1 read as -1": ("unpack_bit1", _unpack_bit1_inverted),
 }
 
 PIN_TESTS = [
@@ -109,6 +122,8 @@ PIN_TESTS = [
     (pins.test_slot2_hand_worked_examples, {}),
     (pins.test_trit5_exhaustive_full_bytes, {}),
     (pins.test_slot2_exhaustive, {}),
+    (pins.test_bit1_hand_worked_examples, {}),
+    (pins.test_bit1_exhaustive, {}),
     (pins.test_layer_bruteforce_several_blocks_and_groups, {}),
     (pins.test_dequant_group_index_along_k, {}),
     (pins.test_matvec_one_hot_closed_form, {}),

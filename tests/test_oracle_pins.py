@@ -231,6 +231,47 @@ def test_slot2_exhaustive():
             assert np.array_equal(oracle.pack_slot2(c)[0], row)
 
 
+def test_bit1_hand_worked_examples():
+    for ex in _golden("packing_examples.json")["bit1_bytes"]:
+        codes = np.zeros((1, 128), dtype=np.int8) - 1
+        codes[0, :8] = ex["codes"]
+        assert int(oracle.pack_bit1(codes)[0, 0]) == ex["byte"], ex
+
+
+def test_bit1_exhaustive():
+    # all 256 bytes: unpack, repack, and the pure-Python packer agree
+    packed = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    codes = oracle.unpack_bit1(packed, 2048)
+    assert set(np.unique(codes).tolist()) == {-1, 1}
+    assert np.array_equal(oracle.pack_bit1(codes), packed)
+    assert bytes(packed.tobytes()) == oracle.pack_bit1_loop(codes)
+    # bit i of byte j is weight 8j + i
+    for b in range(256):
+        want = [1 if (b >> i) & 1 else -1 for i in range(8)]
+        assert codes[0, 8 * b:8 * b + 8].tolist() == want
+
+
+def test_bit1_rejects_zero_and_bad_codes():
+    for bad in (0, 2):
+        c = np.ones((1, 128), dtype=np.int8)
+        c[0, 5] = bad
+        with pytest.raises(ValueError):
+            oracle.pack_bit1(c)
+        with pytest.raises(ValueError):
+            oracle.pack_bit1_loop(c)
+
+
+def test_bit1_holds_the_same_weights_as_the_ternary_packings():
+    rng = np.random.default_rng(5)
+    codes = (2 * rng.integers(0, 2, size=(5, 1024)) - 1).astype(np.int8)
+    scales = rng.standard_normal((5, 8)).astype(np.float16)
+    x = rng.standard_normal((2, 1024)).astype(np.float16)
+    ys = [oracle.matvec_packed(oracle.pack(codes, f), scales, f, x.astype(np.float64), 1024)
+          for f in (oracle.FMT_TRIT5, oracle.FMT_SLOT2, oracle.FMT_BIT1)]
+    assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[1], ys[2])
+    assert np.array_equal(oracle.unpack_bit1(oracle.pack_bit1(codes), 1024), codes)
+
+
 def test_packings_hold_the_same_weights_random():
     rng = np.random.default_rng(3)
     codes = rng.integers(-1, 2, size=(7, 2048)).astype(np.int8)
@@ -254,6 +295,7 @@ def test_packed_sizes_closed_form():
     for n, k in [(1, 128), (1024, 1024), (17408, 5120), (5120, 17408)]:
         assert oracle.packed_bytes(n, k, oracle.FMT_TRIT5) == n * 26 * k // 128
         assert oracle.packed_bytes(n, k, oracle.FMT_SLOT2) == n * k // 4
+        assert oracle.packed_bytes(n, k, oracle.FMT_BIT1) == n * k // 8
     assert oracle.packed_bytes(1024, 1024, oracle.FMT_TRIT5) == 212_992
     assert oracle.packed_bytes(1024, 1024, oracle.FMT_SLOT2) == 262_144
 
@@ -269,6 +311,9 @@ def test_format_densities_against_page_figures():
     trit5_bpw = 8 * oracle.trit5_group_bytes(g) / g + 16 / g
     slot2_bpw = 8 * (g // 4) / g + 16 / g
     assert trit5_bpw == 1.75 and slot2_bpw == 2.125
+    # the binary packing is exactly the page's 1.125 bits per weight
+    bit1_bpw = 8 * oracle.packed_bytes(1, g, oracle.FMT_BIT1) / g + 16 / g
+    assert bit1_bpw == f["binary_effective_bpw"]["value"]
     # both file sizes must describe the same number of weights (same weights,
     # different packing): 5.95 GB / 1.75 bpw vs 7.21 GB / 2.125 bpw
     w_dense = f["dense_trit_file_gb"]["value"] * 8 / trit5_bpw
