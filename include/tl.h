@@ -37,6 +37,10 @@
  *     1.625 code bits + 0.125 scale bits = 1.75 bits per weight.
  *   TL_FMT_SLOT2: each row holds K/4 bytes; bits 2i..2i+1 of byte j hold
  *     d[4j+i].  2.125 bits per weight with the scales.
+ *   TL_FMT_BIT1: codes -1 and +1 only, one bit b = (code + 1) / 2 each: each
+ *     row holds K/8 bytes and bit i of byte j holds b[8j+i].  1.125 bits per
+ *     weight with the scales (page "How Prism ML Squeezed a 27B Model Into
+ *     3.9 GB", list "Two formats ship today").
  *   Scales: binary16 [N, K/128]; weight (n, k) = code * scales[n, k/128].
  *   Signs: int8 [K] of +1/-1; block b of the rotation uses signs[1024b .. +1023].
  */
@@ -67,7 +71,7 @@ typedef enum {
     TL_ERR_DTYPE = 7     /* unknown output dtype                               */
 } tl_status;
 
-enum { TL_FMT_TRIT5 = 0, TL_FMT_SLOT2 = 1 };
+enum { TL_FMT_TRIT5 = 0, TL_FMT_SLOT2 = 1, TL_FMT_BIT1 = 2 };
 enum { TL_F32 = 0, TL_F16 = 1 };
 
 #define TL_BLOCK 1024      /* Hadamard block width                 */
@@ -83,6 +87,7 @@ TL_API int64_t tl_packed_bytes(int64_t N, int64_t K, int32_t fmt);
  * tl_packed_bytes(N, K, fmt) bytes (device).  Requires 1 <= N <= 2^24,
  * K >= 128, K % 128 == 0, K <= TL_MAX_K, N * K <= 2^36.  codes and packed
  * must be 16-byte aligned, bad_count 4-byte aligned.  A code outside {-1, 0, 1} is packed as 0
+ * and counted; with TL_FMT_BIT1 every code other than -1 and +1 is packed as +1
  * and counted: when bad_count (device int32, may be NULL) is given, the
  * number of such codes is ADDED to *bad_count (the caller clears it).
  * packed must not overlap codes.  Bit-exact with the format above. */

@@ -6,7 +6,8 @@ types (int8 codes and signs, binary16 scales and activations).  Both the CPU
 oracle and the HIP library consume the same bytes produced here.
 
 Distributions (workload descriptions of the ternary g128 layer):
-  codes   iid, P(-1) = 0.3, P(0) = 0.4, P(+1) = 0.3
+  codes   iid, P(-1) = 0.3, P(0) = 0.4, P(+1) = 0.3; with ``binary`` (weights
+          of the 1-bit format) iid, P(-1) = P(+1) = 0.5
   scales  |N(0, 0.02)| rounded to binary16, one per 128 weights along K
   signs   Rademacher, one per column of K
   x       N(0, 1) rounded to binary16; with ``outliers`` a Bernoulli(0.01)
@@ -27,7 +28,7 @@ GROUP = 128
 @dataclasses.dataclass
 class LinearInputs:
     signs: np.ndarray    # int8 [K], +-1
-    codes: np.ndarray    # int8 [N, K], {-1, 0, 1}
+    codes: np.ndarray    # int8 [N, K], {-1, 0, 1} ({-1, 1} when binary)
     scales: np.ndarray   # float16 [N, K/128]
     x: np.ndarray        # float16 [M, K]
 
@@ -48,6 +49,10 @@ def draw_codes(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
     return c
 
 
+def draw_binary_codes(rng: np.random.Generator, n: int, k: int) -> np.ndarray:
+    return (rng.integers(0, 2, (n, k), dtype=np.int8) * 2 - 1).astype(np.int8)
+
+
 def draw_scales(rng: np.random.Generator, n: int, k: int, group: int = GROUP) -> np.ndarray:
     return np.abs(0.02 * rng.standard_normal((n, k // group))).astype(np.float16)
 
@@ -61,10 +66,11 @@ def draw_x(rng: np.random.Generator, m: int, k: int, outliers: bool = False) -> 
 
 
 def linear_inputs(n: int, k: int, m: int, *, seed: int = 0, cfg: int = 1, layer: int = 0,
-                  linear: int = 0, outliers: bool = False, group: int = GROUP) -> LinearInputs:
+                  linear: int = 0, outliers: bool = False, group: int = GROUP,
+                  binary: bool = False) -> LinearInputs:
     rng = rng_for(seed, cfg, layer, linear)
     signs = draw_signs(rng, k)
-    codes = draw_codes(rng, n, k)
+    codes = draw_binary_codes(rng, n, k) if binary else draw_codes(rng, n, k)
     scales = draw_scales(rng, n, k, group)
     x = draw_x(rng, m, k, outliers)
     return LinearInputs(signs=signs, codes=codes, scales=scales, x=x)

@@ -42,7 +42,9 @@ def test_packed_bytes():
     assert L.tl_packed_bytes(1, 128, 0) == 26
     assert L.tl_packed_bytes(0, 1024, 0) == -1
     assert L.tl_packed_bytes(4, 100, 0) == -1
-    assert L.tl_packed_bytes(4, 1024, 2) == -1
+    assert L.tl_packed_bytes(4, 1024, 2) == 512          # 1-bit codes: K/8 bytes a row
+    assert L.tl_packed_bytes(17408, 5120, 2) == 17408 * 5120 // 8
+    assert L.tl_packed_bytes(4, 1024, 3) == -1
 
 
 def test_status_strings():
@@ -75,6 +77,7 @@ def test_layer_validation(call):
     assert _gemv(fn, y=A + 0x2000000) == 5
     assert _gemv(fn, y=A + 0x1000000 - 16) == 5
     assert _gemv(fn, y=A + 16) == 5
+    assert _gemv(fn, fmt=2, y=A + 64 * 1024 // 8 - 16) == 5   # 1-bit rows: K/8 bytes
 
 
 def test_linear_validation():

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libtl.so")
 
 FMT_TRIT5 = 0
 FMT_SLOT2 = 1
+FMT_BIT1 = 2
 TL_F32 = 0
 TL_F16 = 1
 BLOCK = 1024

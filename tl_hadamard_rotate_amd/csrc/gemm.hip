@@ -389,6 +389,17 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, c
             return e;
         return launch_gemm_slot2(static_cast<const uint8_t*>(slot2), scales, x, m, n, k, y, y_f16, stream);
     }
+    if (fmt == 2) {
+        // 1-bit codes: rewritten as 2-bit slots (digits 0 and 2) once per call
+        void* slot2 = nullptr;
+        hipError_t e = workspace(kWorkspaceSlot2, stream, size_t(n) * size_t(k / 4), &slot2);
+        if (e != hipSuccess) return e;
+        if ((e = launch_bit1_to_slot2(packed, n, k, static_cast<uint8_t*>(slot2), stream)) != hipSuccess)
+            return e;
+        const uint8_t* s2 = static_cast<const uint8_t*>(slot2);
+        return gemm_slot2_fits(m, n, k) ? launch_gemm_slot2(s2, scales, x, m, n, k, y, y_f16, stream)
+                                        : launch<1>(s2, scales, x, m, n, k, y, y_f16, stream);
+    }
     return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
                     : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
 }

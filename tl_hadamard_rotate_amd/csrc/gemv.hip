@@ -99,6 +99,7 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt, c
         return launch_gemv_m1_slot2(packed, scales, x, n, k, y, y_f16, stream);
     if (fmt == 1) return launch_gemv_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
     if (fmt == 0) return launch_gemv_trit5(packed, scales, x, m, n, k, y, y_f16, stream);
+    if (fmt == 2) return launch_gemv_bit1(packed, scales, x, m, n, k, y, y_f16, stream);
     const unsigned grid = unsigned((n + kWaves - 1) / kWaves);
     for (int64_t m0 = 0; m0 < m; m0 += kMaxTok) {
         const int mt = int(m - m0 < kMaxTok ? m - m0 : kMaxTok);

@@ -2,7 +2,10 @@
 // Formats: 5 trits per byte in base 3 (26 bytes per 128-group) and one 2-bit
 // slot per weight; both hold digit d = code + 1.  The two packings carry the
 // same weights and differ only in layout (page "A 27-billion model that fits
-// in 8.6 GB", paragraph 5).  Bit-exact integer work; offline, once per weight.
+// in 8.6 GB", paragraph 5).  The 1-bit format holds codes -1 and +1 as one bit
+// b = (code + 1) / 2 each, eight to a byte, first weight in the least
+// significant bit (page "How Prism ML Squeezed a 27B Model Into 3.9 GB", list
+// "Two formats ship today").  Bit-exact integer work; offline, once per weight.
 #include "tl_internal.h"
 
 namespace tl {
@@ -63,6 +66,32 @@ __global__ __launch_bounds__(kThreads) void pack_slot2_kernel(
     if (bad_count && bad) atomicAdd(bad_count, int32_t(bad));
 }
 
+// One thread per output dword of the 1-bit format (32 codes in, 4 bytes out);
+// codes other than -1 and +1 become bit 1 (code +1) and are counted.
+__global__ __launch_bounds__(kThreads) void pack_bit1_kernel(
+    const int8_t* __restrict__ codes, int64_t n, int64_t k, uint8_t* __restrict__ packed,
+    int32_t* __restrict__ bad_count) {
+    const int64_t total = n * k / 32;
+    uint32_t bad = 0;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const int4* src = reinterpret_cast<const int4*>(codes) + 2 * idx;
+        uint32_t word = 0;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int4 raw = src[half];
+            const int8_t* c = reinterpret_cast<const int8_t*>(&raw);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                bad += (c[i] != -1) & (c[i] != 1);
+                word |= uint32_t(c[i] != -1) << (16 * half + i);
+            }
+        }
+        reinterpret_cast<uint32_t*>(packed)[idx] = word;
+    }
+    if (bad_count && bad) atomicAdd(bad_count, int32_t(bad));
+}
+
 __global__ __launch_bounds__(kThreads) void unpack_trit5_kernel(
     const uint8_t* __restrict__ packed, int64_t n, int64_t k, int8_t* __restrict__ codes) {
     const int64_t row_bytes = (k / kGroup) * kTrit5GroupBytes;
@@ -100,6 +129,43 @@ __global__ __launch_bounds__(kThreads) void unpack_slot2_kernel(
             out |= (uint32_t(uint8_t(int8_t(int(d) - 1)))) << (8 * i);
         }
         reinterpret_cast<uint32_t*>(codes)[idx] = out;
+    }
+}
+
+// One thread per input byte of the 1-bit format: 8 codes out.
+__global__ __launch_bounds__(kThreads) void unpack_bit1_kernel(
+    const uint8_t* __restrict__ packed, int64_t n, int64_t k, int8_t* __restrict__ codes) {
+    const int64_t total = n * k / 8;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const uint32_t b = packed[idx];
+        uint32_t out[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            out[i >> 2] |= ((b >> i) & 1u ? 0x01u : 0xFFu) << (8 * (i & 3));
+        reinterpret_cast<uint2*>(codes)[idx] = uint2{out[0], out[1]};
+    }
+}
+
+// One thread per input dword of the 1-bit format: its 32 bits b become the
+// 2-bit digits 2b (code -1 -> digit 0, +1 -> digit 2), two output dwords.
+__global__ __launch_bounds__(kThreads) void bit1_to_slot2_kernel(
+    const uint8_t* __restrict__ bit1, int64_t total, uint8_t* __restrict__ slot2) {
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const uint32_t w = reinterpret_cast<const uint32_t*>(bit1)[idx];
+        uint32_t out[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // spread 16 bits to the even bit positions of a dword, then move them up one
+            uint32_t v = (w >> (16 * h)) & 0xFFFFu;
+            v = (v | (v << 8)) & 0x00FF00FFu;
+            v = (v | (v << 4)) & 0x0F0F0F0Fu;
+            v = (v | (v << 2)) & 0x33333333u;
+            v = (v | (v << 1)) & 0x55555555u;
+            out[h] = v << 1;
+        }
+        reinterpret_cast<uint2*>(slot2)[idx] = uint2{out[0], out[1]};
     }
 }
 
@@ -162,6 +228,9 @@ hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt, uint8
         const int64_t total = n * (k / kGroup) * kTrit5GroupBytes;
         hipLaunchKernelGGL(pack_trit5_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
                            codes, n, k, packed, bad_count);
+    } else if (fmt == 2) {
+        hipLaunchKernelGGL(pack_bit1_kernel, dim3(grid_for(n * k / 32)), dim3(kThreads), 0, stream,
+                           codes, n, k, packed, bad_count);
     } else {
         const int64_t total = n * k / 16;
         hipLaunchKernelGGL(pack_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
@@ -177,12 +246,23 @@ hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uin
     return hipGetLastError();
 }
 
+hipError_t launch_bit1_to_slot2(const uint8_t* bit1, int64_t n, int64_t k, uint8_t* slot2,
+                               hipStream_t stream) {
+    const int64_t total = n * k / 32;
+    hipLaunchKernelGGL(bit1_to_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                       bit1, total, slot2);
+    return hipGetLastError();
+}
+
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int fmt, int8_t* codes,
                          hipStream_t stream) {
     if (fmt == 0) {
         const int64_t total = n * (k / kGroup) * kTrit5GroupBytes;
         hipLaunchKernelGGL(unpack_trit5_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
                            packed, n, k, codes);
+    } else if (fmt == 2) {
+        hipLaunchKernelGGL(unpack_bit1_kernel, dim3(grid_for(n * k / 8)), dim3(kThreads), 0,
+                           stream, packed, n, k, codes);
     } else {
         const int64_t total = n * k / 4;
         hipLaunchKernelGGL(unpack_slot2_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,

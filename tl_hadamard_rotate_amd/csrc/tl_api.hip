@@ -22,8 +22,12 @@ bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     return a0 < b0 + uintptr_t(b_bytes) && b0 < a0 + uintptr_t(a_bytes);
 }
 
+bool known_fmt(int32_t fmt) {
+    return fmt == TL_FMT_TRIT5 || fmt == TL_FMT_SLOT2 || fmt == TL_FMT_BIT1;
+}
+
 int64_t row_bytes(int64_t k, int32_t fmt) {
-    return fmt == TL_FMT_TRIT5 ? (k / TL_GROUP) * 26 : k / 4;
+    return fmt == TL_FMT_TRIT5 ? (k / TL_GROUP) * 26 : fmt == TL_FMT_BIT1 ? k / 8 : k / 4;
 }
 
 tl_status launched(hipError_t e) {
@@ -48,7 +52,7 @@ tl_status check_layer(const uint8_t* packed, const uint16_t* scales, int32_t fmt
                       int32_t y_dtype) {
     if (!packed || !scales || !x_rot || !y) return TL_ERR_NULL;
     if (!layer_shape_ok(m, n, k)) return TL_ERR_SHAPE;
-    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (!known_fmt(fmt)) return TL_ERR_FORMAT;
     if (y_dtype != TL_F32 && y_dtype != TL_F16) return TL_ERR_DTYPE;
     if (!aligned16(packed) || !aligned16(scales) || !aligned16(x_rot) || !aligned16(y))
         return TL_ERR_ALIGN;
@@ -65,7 +69,7 @@ extern "C" {
 
 int64_t tl_packed_bytes(int64_t N, int64_t K, int32_t fmt) {
     if (N < 1 || K < TL_GROUP || K % TL_GROUP != 0) return -1;
-    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return -1;
+    if (!known_fmt(fmt)) return -1;
     return N * row_bytes(K, fmt);
 }
 
@@ -73,7 +77,7 @@ tl_status tl_pack(const int8_t* codes, int64_t N, int64_t K, int32_t fmt, uint8_
                   int32_t* bad_count, hipStream_t stream) {
     if (!codes || !packed) return TL_ERR_NULL;
     if (!pack_shape_ok(N, K)) return TL_ERR_SHAPE;
-    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (!known_fmt(fmt)) return TL_ERR_FORMAT;
     if (!aligned16(codes) || !aligned16(packed)) return TL_ERR_ALIGN;
     if (bad_count && (reinterpret_cast<uintptr_t>(bad_count) & 3u)) return TL_ERR_ALIGN;
     const int64_t pb = N * row_bytes(K, fmt);
@@ -87,7 +91,7 @@ tl_status tl_unpack(const uint8_t* packed, int64_t N, int64_t K, int32_t fmt, in
                     hipStream_t stream) {
     if (!codes || !packed) return TL_ERR_NULL;
     if (!pack_shape_ok(N, K)) return TL_ERR_SHAPE;
-    if (fmt != TL_FMT_TRIT5 && fmt != TL_FMT_SLOT2) return TL_ERR_FORMAT;
+    if (!known_fmt(fmt)) return TL_ERR_FORMAT;
     if (!aligned16(codes) || !aligned16(packed)) return TL_ERR_ALIGN;
     if (overlap(packed, N * row_bytes(K, fmt), codes, N * K)) return TL_ERR_ALIAS;
     return launched(tl::launch_unpack(packed, N, K, fmt, codes, stream));

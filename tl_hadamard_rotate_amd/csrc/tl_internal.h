@@ -45,6 +45,13 @@ hipError_t workspace(int kind, hipStream_t stream, size_t bytes, void** out);
 // [n][k/4] bytes.
 hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uint8_t* slot2,
                                  hipStream_t stream);
+// The 1-bit packing rewritten as 2-bit slots (digit 2b), row-major [n][k/4] bytes.
+hipError_t launch_bit1_to_slot2(const uint8_t* bit1, int64_t n, int64_t k, uint8_t* slot2,
+                                hipStream_t stream);
+// Decode GEMV of the 1-bit packing (any m; tokens in launches of at most 16)
+hipError_t launch_gemv_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                            int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                            hipStream_t stream);
 // Prefill GEMM of the 2-bit-slot packing with the weights decoded in
 // registers; usable when gemm_slot2_fits(m, n, k)
 bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
