@@ -23,10 +23,12 @@ is the one those counters were taken from.
 Extras: the other packing, the prefill GEMM sweep, batched decode over the
 attention projections, the rotation at prefill size, the 64-layer weight
 stream (one rotation per linear, and one per input with q|k|v and gate|up
-concatenated), and the CPU oracle on a bounded sample.
+concatenated), the decode step with 1-bit weights, and the CPU oracle on a
+bounded sample.
 
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
+    python bench.py --profile-pass [--fmt slot2|trit5|bit1]
 """
 from __future__ import annotations
 
@@ -46,7 +48,7 @@ METRIC = "ternary GEMV GB/s (% HBM peak) + prefill GEMM TFLOP/s at 27B-class sha
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 STEP_LINEARS = ("gate", "up", "down")
-FMT_NAMES = {"trit5": 0, "slot2": 1}
+FMT_NAMES = {"trit5": 0, "slot2": 1, "bit1": 2}
 KERNEL_SRC = {0: "gemv_trit5.hip", 1: "gemv_m1.hip"}
 
 
@@ -54,19 +56,23 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def code_bytes(n: int, k: int, fmt: int) -> int:
+    """Packed code bytes of an N x K weight: 26 per 128-group (dense trits),
+    K/4 a row (2-bit slots) or K/8 a row (1-bit codes)."""
+    return n * (k // 128) * 26 if fmt == 0 else n * k // 8 if fmt == 2 else n * k // 4
+
+
 def linear_bytes(n: int, k: int, m: int, fmt: int) -> int:
     """Algorithmic bytes of one fused tl_linear launch: codes + scales +
     unrotated binary16 activations and int8 signs read, rotated activations
     (binary16) and fp32 outputs written."""
-    code_bytes = n * (k // 128) * 26 if fmt == 0 else n * k // 4
-    return code_bytes + n * (k // 128) * 2 + m * k * 2 + k + m * k * 2 + m * n * 4
+    return code_bytes(n, k, fmt) + n * (k // 128) * 2 + m * k * 2 + k + m * k * 2 + m * n * 4
 
 
 def gemv_bytes(n: int, k: int, m: int, fmt: int) -> int:
     """Algorithmic bytes of one GEMV launch: packed codes + binary16 scales +
     binary16 activations read, fp32 outputs written."""
-    code_bytes = n * (k // 128) * 26 if fmt == 0 else n * k // 4
-    return code_bytes + n * (k // 128) * 2 + m * k * 2 + m * n * 4
+    return code_bytes(n, k, fmt) + n * (k // 128) * 2 + m * k * 2 + m * n * 4
 
 
 def rotate_bytes(m: int, k: int) -> int:
@@ -99,7 +105,8 @@ def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
     lins = []
     for name in STEP_LINEARS:
         k, n = synth.SHAPES[name]
-        inp = synth.linear_inputs(n, k, 1, seed=0, cfg=2, layer=0, linear=synth.LINEAR_ID[name])
+        inp = synth.linear_inputs(n, k, 1, seed=0, cfg=2, layer=0, linear=synth.LINEAR_ID[name],
+                                  binary=fmt == 2)
         codes = torch.from_numpy(inp.codes).to(dev)
         packed = tl.pack(codes, fmt)
         del codes
@@ -395,6 +402,44 @@ def bench_stream_shared(torch, tl, synth, dev, fmt, stream, reps=5):
             "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
 
 
+def bench_bit1(torch, tl, synth, dev, stream, copies, steps, warmup):
+    """The decode step with 1-bit weights (codes -1/+1, g128 scales): per
+    projection the rotation + the 1-bit GEMV (tl_linear, two launches), the
+    GEMV alone on rotated activations, and the GEMV at M = 1, 4, 16 on gate;
+    weights cycled over `copies` buffers, launches captured in HIP graphs."""
+    fmt = 2
+    lins = build_step_inputs(torch, tl, synth, dev, fmt, copies)
+    with torch.cuda.stream(stream):
+        sg = capture(torch, lambda c: step_fn(tl, lins, fmt, c), copies, stream)
+        gg = capture(torch, lambda c: gemv_fn(tl, lins, fmt, c), copies, stream)
+    ms = timed_replays(torch, sg, steps, warmup, stream) / steps
+    reps = max(steps, 3 * copies)
+    g_us = timed_replays(torch, gg, reps, warmup, stream) * 1e3 / (3 * reps)
+    sbytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
+    g_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+    out = {"step_GBs": round(sbytes / (ms * 1e-3) / 1e9, 1), "ms_per_step": round(ms, 5),
+           "step_bytes": sbytes, "gemv_avg_launch_us": round(g_us, 3),
+           "gemv_GBs": round(g_bytes / (g_us * 1e-6) / 1e9, 1), "gate_batched": []}
+    del sg, gg
+    gate = lins[0]
+    k, n = gate["k"], gate["n"]
+    for m in (1, 4, 16):
+        xm = torch.randn((m, k), generator=torch.Generator(device="cpu").manual_seed(m)).to(
+            torch.float16).to(dev)
+        ym = torch.empty((m, n), dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            gm = capture(torch, lambda c: tl.gemv(gate["packs"][c], gate["scales"][c], fmt, xm,
+                                                  out=ym), copies, stream)
+        r = max(steps, copies)
+        us = timed_replays(torch, gm, r, warmup, stream) * 1e3 / r
+        out["gate_batched"].append({"M": m, "us": round(us, 3),
+                                    "GBs": round(gemv_bytes(n, k, m, fmt) / (us * 1e-6) / 1e9, 1)})
+        del gm
+    del lins
+    torch.cuda.empty_cache()
+    return out
+
+
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
     256 MiB written per launch), then 10 eager decode steps (per projection
@@ -482,6 +527,10 @@ def main(argv=None) -> int:
 
     dev = torch.device("cuda:0")
     fmt = FMT_NAMES[args.fmt]
+    if fmt == 2 and not args.profile_pass:
+        print("--fmt bit1 applies to --profile-pass; the 1-bit decode step is measured in the "
+              "extras of the default run", file=sys.stderr)
+        return 2
     stream = torch.cuda.Stream(dev)
     if args.profile_pass:
         return profile_pass(torch, tl, synth, dev, fmt)
@@ -554,6 +603,9 @@ def main(argv=None) -> int:
         log("64-layer weight stream, one rotation per input (q|k|v and gate|up concatenated)")
         extra["weight_stream_shared_rotation"] = bench_stream_shared(torch, tl, synth, dev, fmt,
                                                                      stream)
+        log("decode step with 1-bit weights")
+        extra["bit1_decode"] = bench_bit1(torch, tl, synth, dev, stream, args.copies, args.steps,
+                                          args.warmup)
 
     cpu = None
     if not args.no_cpu_baseline:

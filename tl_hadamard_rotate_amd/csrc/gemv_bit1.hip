@@ -7,9 +7,11 @@
 //
 // with b the stored bits and X[m, g] the group sums of the activations.
 //
-// Lanes are weight rows: a workgroup holds 64 rows, its waves split the K
-// groups between them and add their partial sums through LDS in wave order
-// (bitwise deterministic).
+// A workgroup owns 16 weight rows.  A step covers 4 groups: lane 16q + r
+// takes row r and group 4s + q of step s, so one 16-byte load per lane reads
+// 64 contiguous bytes of each of the 16 rows, and the 16 lanes of a DPP row
+// share one group.  The waves of a workgroup split the steps and add their
+// partial sums through LDS in a fixed order (bitwise deterministic).
 //
 // Bits j and j + 16 of a weight dword meet the activation pair
 // (x[32d + j], x[32d + j + 16]).  A bit at position 10..14 of a binary16
@@ -22,12 +24,12 @@
 // used: v_dot2_f32_f16 adds products with a subnormal operand to the
 // accumulator inexactly.
 //
-// Each launch first writes its tokens' activations to LDS as pairs, with the
-// group sums.  The 16 pairs of one weight dword then sit in one VGPR (one
-// ds_read_b128 gives a lane its pair j = lane mod 16 of the group's 4 dwords),
-// and v_dot2c_f32_f16 reads pair j for every lane through the DPP
-// row_newbcast:j operand: per 2 weights one v_and (shared by all tokens) and
-// one v_dot2c per token.
+// Lane r of a DPP row holds activation pair r of the group's dword d (one
+// VGPR per dword, built from two 16-bit loads), and v_dot2c_f32_f16 reads
+// pair j for every lane of the row through the DPP row_newbcast:j operand:
+// per 2 weights one v_and (shared by all tokens) and one v_dot2c per token.
+// X_g is a v_dot2 of the lane's pairs with (1, 1) and a butterfly over the
+// row of 16 lanes.
 #include <hip/hip_fp16.h>
 
 #include "tl_internal.h"
