@@ -35,6 +35,11 @@ Readings taken where the pages are silent (all listed in the design doc):
   two bits each, least significant first.  BIT1 (codes -1 and +1 only):
   byte j holds bits b[8j..8j+7], least significant first, code = 2b - 1.
 * Scales: binary16 array [N, K/128]; a weight is c * S.
+* Weight-side quantisation (the pages' pipeline rotates, then rounds to
+  -1/0/+1 with one scale per 128 by GPTQ on calibration data; without data
+  the plain stand-in is round to nearest with an absmean scale):
+  S = binary16(mean |w'| over the group), c = clip(rint(w' / S), -1, 1)
+  (ties to even, so |w'| = S/2 gives 0), c = 0 where S = 0.
 
 Parity status of every function here is recorded in the design doc; the pins live
 in tests/test_oracle_*.py.
@@ -325,6 +330,46 @@ def fold_weights(w: np.ndarray, signs: np.ndarray, block: int = BLOCK) -> np.nda
     """Fold the rotation into real-valued weight rows: every row gets the same
     map as the activations, so fold(w) . R(x) = w . x."""
     return rotate(w, signs, block)
+
+
+# ---------------------------------------------------------------------------
+# Weight-side quantisation: fold the rotation into the rows, round to ternary
+# ---------------------------------------------------------------------------
+
+def quantize_ternary(w_rot: np.ndarray, group: int = GROUP):
+    """Round already rotated weight rows to ternary g128.
+
+    Page "OpenBonsai", section "How it works", step 2: every large linear is
+    rounded to -1, 0 or +1 with one scale per 128 weights (there by GPTQ on
+    calibration data; here by rounding to nearest, the data-free reading).
+    Page "A 27-billion model that fits in 8.6 GB", paragraph 2: the scale is
+    an FP16 number shared by the 128 weights.
+
+    Per group: S = mean of |w| in fp64, rounded to binary16 (nearest even);
+    c = rint(w / S) (half to even) clipped to [-1, 1], and c = 0 where S is 0.
+    Returns (codes int8 [N, K], scales float16 [N, K/group])."""
+    w = np.asarray(w_rot, dtype=np.float64)
+    n, k = w.shape
+    if k % group:
+        raise ValueError("K must be a multiple of the group")
+    g = w.reshape(n, k // group, group)
+    scales = np.abs(g).mean(axis=2).astype(np.float16)
+    s = scales.astype(np.float64)[:, :, None]
+    codes = np.zeros_like(g)
+    nz = np.broadcast_to(s != 0.0, g.shape)
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        q = np.clip(np.rint(g / s), -1.0, 1.0)
+    codes[nz] = q[nz]
+    return codes.reshape(n, k).astype(np.int8), scales
+
+
+def quantize_weights(w: np.ndarray, signs: np.ndarray, block: int = BLOCK,
+                     group: int = GROUP):
+    """The weight side of the layer: rotate the real-valued rows with the
+    activations' signed transform (page "OpenBonsai", section "How it works",
+    step 1; Persian page, paragraph 2: the rotation is folded into the
+    weights), then round them to ternary g128 (``quantize_ternary``)."""
+    return quantize_ternary(fold_weights(w, signs, block), group)
 
 
 # ---------------------------------------------------------------------------

@@ -10,7 +10,8 @@ from tests import test_oracle_pins as pins
 
 _orig = {name: getattr(ref, name) for name in
          ("hadamard", "rotate", "dequant", "matvec", "pack_trit5", "unpack_trit5",
-          "pack_slot2", "unpack_slot2", "pack_bit1", "unpack_bit1")}
+          "pack_slot2", "unpack_slot2", "pack_bit1", "unpack_bit1", "quantize_ternary",
+          "fold_weights")}
 
 
 def _rotate_signs_last(x, signs, block=ref.BLOCK):
@@ -97,6 +98,38 @@ def _unpack_bit1_inverted(packed, k):
     return (-_orig["unpack_bit1"](packed, k)).astype(np.int8)
 
 
+def _quantize_with(scale_fn, round_fn=np.rint, clip=True, to_half=True):
+    def q(w_rot, group=ref.GROUP):
+        w = np.asarray(w_rot, dtype=np.float64)
+        n, k = w.shape
+        g = w.reshape(n, k // group, group)
+        s = scale_fn(np.abs(g), w)
+        if to_half:
+            s = s.astype(np.float16)
+        sd = np.asarray(s, dtype=np.float64)[:, :, None]
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = round_fn(g / sd)
+        if clip:
+            r = np.clip(r, -1, 1)
+        r = np.where(sd != 0, r, 0)
+        return r.reshape(n, k).astype(np.int8), np.asarray(s).astype(np.float16)
+    return q
+
+
+_mean_scale = lambda a, w: a.mean(axis=2)
+_max_scale = lambda a, w: a.max(axis=2)
+_row_scale = lambda a, w: np.repeat(np.abs(w).mean(axis=1)[:, None], a.shape[1], axis=1)
+_half_away = lambda v: np.trunc(v + 0.5 * np.sign(v))
+
+
+def _quantize_weights_unrotated(w, signs, block=ref.BLOCK, group=ref.GROUP):
+    return ref.quantize_ternary(np.asarray(w, dtype=np.float64), group)
+
+
+def _fold_weights_unsigned(w, signs, block=ref.BLOCK):
+    return _orig["rotate"](w, np.ones_like(np.asarray(signs)), block)
+
+
 MUTATIONS = {
     "rotate: signs after H": ("rotate", _rotate_signs_last),
     "rotate: 1/n instead of 1/sqrt(n)": ("rotate", _rotate_wrong_norm),
@@ -109,6 +142,15 @@ MUTATIONS = {
     "pack_slot2: two's complement slots": ("pack_slot2", _pack_slot2_signed),
     "pack_bit1: most significant bit first": ("pack_bit1", _pack_bit1_msb_first),
     "unpack_bit1: bit 1 read as -1": ("unpack_bit1", _unpack_bit1_inverted),
+    "quantize: absmax scale": ("quantize_ternary", _quantize_with(_max_scale)),
+    "quantize: one scale per row": ("quantize_ternary", _quantize_with(_row_scale)),
+    "quantize: no clipping": ("quantize_ternary", _quantize_with(_mean_scale, clip=False)),
+    "quantize: ties away from zero": ("quantize_ternary",
+                                      _quantize_with(_mean_scale, round_fn=_half_away)),
+    "quantize: scale kept in fp64": ("quantize_ternary",
+                                     _quantize_with(_mean_scale, to_half=False)),
+    "quantize_weights: rotation skipped": ("quantize_weights", _quantize_weights_unrotated),
+    "fold_weights: signs dropped": ("fold_weights", _fold_weights_unsigned),
 }
 
 PIN_TESTS = [
@@ -129,6 +171,10 @@ PIN_TESTS = [
     (pins.test_matvec_one_hot_closed_form, {}),
     (pins.test_matvec_orientation_nonsymmetric, {}),
     (pins.test_fold_invariant_and_negative, {}),
+    (pins.test_quantize_hand_worked_groups, {}),
+    (pins.test_quantize_scale_is_nearest_binary16_to_exact_mean_and_codes_nearest, {}),
+    (pins.test_quantize_invariances, {}),
+    (pins.test_quantize_weights_one_hot_closed_form, {}),
 ]
 
 

@@ -485,3 +485,107 @@ def test_fp16_ulp_matches_numpy_spacing():
     vals = np.array([0.0, 1e-7, 6e-5, 6.2e-5, 0.3, 1.0, 1.5, 2.0, 3.9, 1000.0, 60000.0])
     want = np.spacing(vals.astype(np.float16)).astype(np.float64)
     assert np.array_equal(oracle.fp16_ulp(vals.astype(np.float16)), want)
+
+
+# ---------------------------------------------------------------------------
+# Weight quantiser (fold the rotation into the rows, round to ternary g128)
+# ---------------------------------------------------------------------------
+
+def _runs(runs):
+    return np.concatenate([np.full(c, v, dtype=np.float64) for v, c in runs])
+
+
+def test_quantize_hand_worked_groups():
+    """Groups worked by hand (tests/golden/quantize_examples.json), placed one
+    after the other in a single row, so a scale taken over the wrong span
+    shows too."""
+    groups = _golden("quantize_examples.json")["groups"]
+    row = np.concatenate([_runs(g["runs"]) for g in groups])[None, :]
+    codes, scales = oracle.quantize_ternary(row)
+    assert codes.dtype == np.int8 and scales.dtype == np.float16
+    assert scales.shape == (1, len(groups))
+    for i, g in enumerate(groups):
+        assert float(scales[0, i]) == g["scale"], (i, g["work"])
+        assert np.array_equal(codes[0, 128 * i:128 * (i + 1)], _runs(g["codes"])), (i, g["work"])
+
+
+def _fp16_neighbours(v):
+    h = np.float16(v)
+    return [np.nextafter(h, np.float16(-np.inf)), h, np.nextafter(h, np.float16(np.inf))]
+
+
+def test_quantize_scale_is_nearest_binary16_to_exact_mean_and_codes_nearest():
+    """Exact rational brute force on small random rows: the scale is the
+    binary16 number nearest the exact mean of |w| (ties to the even mantissa),
+    and each code is the point of {-S, 0, S} nearest w (0 on a tie with S/2)."""
+    rng = np.random.default_rng(11)
+    w = rng.standard_normal((3, 256)) * np.array([[0.02], [1.0], [300.0]])
+    w[1, :128] = np.round(w[1, :128] * 8) / 8      # many exact ties possible
+    codes, scales = oracle.quantize_ternary(w)
+    for n in range(w.shape[0]):
+        for g in range(2):
+            seg = w[n, 128 * g:128 * (g + 1)]
+            mean = sum(Fraction(float(abs(v))) for v in seg) / 128
+            s = scales[n, g]
+            dist = abs(Fraction(float(s)) - mean)
+            for nb in _fp16_neighbours(float(s)):
+                d_nb = abs(Fraction(float(nb)) - mean)
+                assert dist <= d_nb
+                if dist == d_nb and nb != s:   # a tie between two binary16 numbers
+                    assert int(np.float16(s).view(np.uint16)) % 2 == 0
+            S = Fraction(float(s))
+            for k in range(128):
+                v = Fraction(float(seg[k]))
+                c = int(codes[n, 128 * g + k])
+                dists = {cc: abs(v - cc * S) for cc in (-1, 0, 1)}
+                best = min(dists.values())
+                assert dists[c] == best, (n, g, k)
+                if list(dists.values()).count(best) > 1:
+                    assert c == 0
+
+
+def test_quantize_invariances():
+    """Negating the weights negates the codes; a power-of-two factor scales S
+    exactly; permuting a group permutes its codes; zero groups give S = 0."""
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((4, 512)) * 0.03
+    c, s = oracle.quantize_ternary(w)
+    c2, s2 = oracle.quantize_ternary(-w)
+    assert np.array_equal(c2, -c) and np.array_equal(s2, s)
+    for e in (3, -3):
+        c3, s3 = oracle.quantize_ternary(w * 2.0 ** e)
+        assert np.array_equal(c3, c)
+        assert np.array_equal(s3.astype(np.float64), s.astype(np.float64) * 2.0 ** e)
+    perm = rng.permutation(128)
+    wp = w.copy()
+    wp[:, 128:256] = w[:, 128:256][:, perm]
+    c4, s4 = oracle.quantize_ternary(wp)
+    assert np.array_equal(s4, s)
+    assert np.array_equal(c4[:, 128:256], c[:, 128:256][:, perm])
+    wz = w.copy()
+    wz[2, 256:384] = 0.0
+    c5, s5 = oracle.quantize_ternary(wz)
+    assert s5[2, 2] == 0 and not c5[2, 256:384].any()
+
+
+def test_quantize_weights_one_hot_closed_form():
+    """A weight row e_k rotates to s_k * H[:, k mod 1024] / 32 on its block
+    (Sylvester H[i, j] = (-1)^popcount(i AND j)): every group of that block has
+    S = 1/32 and codes s_k * H[i, k mod 1024]; the other blocks are zero."""
+    k_total = 3072
+    rng = np.random.default_rng(8)
+    signs = (rng.integers(0, 2, k_total) * 2 - 1).astype(np.int8)
+    ks = [0, 5, 1023, 1024 + 77, 2048 + 600]
+    w = np.zeros((len(ks), k_total))
+    for r, k in enumerate(ks):
+        w[r, k] = 1.0
+    codes, scales = oracle.quantize_weights(w, signs)
+    h = _popcount_hadamard(1024)
+    for r, k in enumerate(ks):
+        b, j = divmod(k, 1024)
+        want = np.zeros(k_total, dtype=np.int8)
+        want[1024 * b:1024 * (b + 1)] = (signs[k] * h[:, j]).astype(np.int8)
+        assert np.array_equal(codes[r], want), k
+        want_s = np.zeros(k_total // 128)
+        want_s[8 * b:8 * (b + 1)] = 1.0 / 32
+        assert np.array_equal(scales[r].astype(np.float64), want_s), k
