@@ -23,8 +23,8 @@ is the one those counters were taken from.
 Extras: the other packing, the prefill GEMM sweep, batched decode over the
 attention projections, the rotation at prefill size, the 64-layer weight
 stream (one rotation per linear, and one per input with q|k|v and gate|up
-concatenated), the decode step with 1-bit weights, and the CPU oracle on a
-bounded sample.
+concatenated), the weight quantiser, the decode step with 1-bit weights, and
+the CPU oracle on a bounded sample.
 
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
@@ -440,6 +440,31 @@ def bench_bit1(torch, tl, synth, dev, stream, copies, steps, warmup):
     return out
 
 
+def quantize_bytes(n: int, k: int) -> int:
+    """Algorithmic bytes of one tl_quantize launch: fp32 weights and int8
+    signs read, int8 codes and binary16 scales written."""
+    return n * k * 4 + k + n * k + n * (k // 128) * 2
+
+
+def bench_quantize(torch, tl, synth, dev, reps=10):
+    """The weight quantiser (rotation folded in, round to ternary g128) on the
+    gate and down shapes: average launch time between HIP events, GB/s."""
+    out = []
+    for name in ("gate", "down"):
+        k, n = synth.SHAPES[name]
+        gen = torch.Generator(device="cpu").manual_seed(k)
+        w = (0.02 * torch.randn((n, k), generator=gen)).to(dev)
+        s = (torch.randint(0, 2, (k,), generator=gen) * 2 - 1).to(torch.int8).to(dev)
+        tl.quantize(w, s)
+        torch.cuda.synchronize()
+        ms = _event_time(torch, lambda i: tl.quantize(w, s), reps)
+        out.append({"linear": name, "N": n, "K": k, "us": round(ms * 1e3, 2),
+                    "GBs": round(quantize_bytes(n, k) / (ms * 1e-3) / 1e9, 1)})
+        del w
+        torch.cuda.empty_cache()
+    return out
+
+
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
     256 MiB written per launch), then 10 eager decode steps (per projection
@@ -603,6 +628,8 @@ def main(argv=None) -> int:
         log("64-layer weight stream, one rotation per input (q|k|v and gate|up concatenated)")
         extra["weight_stream_shared_rotation"] = bench_stream_shared(torch, tl, synth, dev, fmt,
                                                                      stream)
+        log("weight quantiser (rotation folded in), gate and down")
+        extra["quantize"] = bench_quantize(torch, tl, synth, dev)
         log("decode step with 1-bit weights")
         extra["bit1_decode"] = bench_bit1(torch, tl, synth, dev, stream, args.copies, args.steps,
                                           args.warmup)

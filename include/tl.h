@@ -167,6 +167,23 @@ TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_
                     const uint16_t* x, const int8_t* signs, int64_t M, int64_t N, int64_t K,
                     uint16_t* x_rot, void* y, int32_t y_dtype, hipStream_t stream);
 
+/* Quantise real-valued weight rows to ternary g128, the rotation folded in
+ * (page "OpenBonsai", section "How it works", steps 1 and 2: rotate with the
+ * signed Hadamard transform, then round to -1, 0, +1 with one scale per 128;
+ * the page rounds by GPTQ on calibration data, this call by round to nearest;
+ * page "A 27-billion model that fits in 8.6 GB", paragraph 2: FP16 scales).
+ *   w'  = R(w) row by row (the map tl_hadamard_rotate applies, fp32 here);
+ *   S   = the binary16 nearest to the mean of |w'| over each group of 128;
+ *   c   = rint(w' / S) clipped to [-1, 1], ties to even (|w'| = S/2 gives 0),
+ *         c = 0 where S = 0.
+ * w: fp32 [N, K]; signs: int8 [K] (negative = -1); codes: int8 [N, K];
+ * scales: binary16 [N, K/128]; all device memory, 16-byte aligned.
+ * 1 <= N <= 2^24, K % 1024 == 0, 1024 <= K <= TL_MAX_K, N * K <= 2^36.
+ * codes and scales must not overlap each other, w or signs.  The result is
+ * bitwise reproducible; codes then go to tl_pack. */
+TL_API tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int64_t K,
+                             int8_t* codes, uint16_t* scales, hipStream_t stream);
+
 /* Static name of a status code ("TL_OK", ...). */
 TL_API const char* tl_status_str(tl_status status);
 

@@ -23,7 +23,7 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for need in ("tl_pack", "tl_hadamard_rotate", "tl_gemv", "tl_gemm"):
+    for need in ("tl_pack", "tl_hadamard_rotate", "tl_gemv", "tl_gemm", "tl_linear", "tl_quantize"):
         assert need in names
 
 
@@ -131,3 +131,23 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError):
         tl.hadamard_rotate(torch.zeros((1, 1024), dtype=torch.float16),
                            torch.ones(1024, dtype=torch.int8))
+
+
+def test_quantize_validation():
+    f = tl.lib().tl_quantize
+    W, G, C, S = A, A + 0x1000000, A + 0x2000000, A + 0x3000000
+
+    def call(w=W, signs=G, n=4, k=1024, codes=C, scales=S):
+        return f(w, signs, n, k, codes, scales, NULL)
+
+    assert call(w=NULL) == 1
+    assert call(scales=NULL) == 1
+    assert call(k=1000) == 2
+    assert call(k=512) == 2
+    assert call(n=0) == 2
+    assert call(w=W + 4) == 4
+    assert call(codes=C + 8) == 4
+    assert call(codes=W + 16) == 5                 # codes over the weights (16 KB)
+    assert call(codes=G - 16) == 5                 # over the signs
+    assert call(scales=C + 4096 - 16) == 5         # scales over the codes (4 KB)
+    assert call(scales=W) == 5

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "tl_gemv": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p]),
+            "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }
@@ -142,6 +143,21 @@ def hadamard_rotate(x: torch.Tensor, signs: torch.Tensor,
     _check("tl_hadamard_rotate",
            lib().tl_hadamard_rotate(_ptr(x), _ptr(signs), m, k, _ptr(out), _stream(x)))
     return out
+
+
+def quantize(w: torch.Tensor, signs: torch.Tensor):
+    """Rotate fp32 weight rows w [N, K] with the signed transform and round
+    them to ternary g128: returns (codes int8 [N, K], scales float16 [N, K/128])."""
+    _need(w, "w", torch.float32, 2)
+    _need(signs, "signs", torch.int8, 1)
+    n, k = w.shape
+    if signs.shape[0] != k:
+        raise ValueError("signs must have K entries")
+    codes = torch.empty((n, k), dtype=torch.int8, device=w.device)
+    scales = torch.empty((n, k // 128), dtype=torch.float16, device=w.device)
+    _check("tl_quantize", lib().tl_quantize(_ptr(w), _ptr(signs), n, k, _ptr(codes), _ptr(scales),
+                                            _stream(w)))
+    return codes, scales
 
 
 def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out):

@@ -150,6 +150,21 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
     return launched(e);
 }
 
+tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int64_t K, int8_t* codes,
+                      uint16_t* scales, hipStream_t stream) {
+    if (!w || !signs || !codes || !scales) return TL_ERR_NULL;
+    if (!(N >= 1 && N <= kMaxRows && K >= TL_BLOCK && K % TL_BLOCK == 0 && K <= TL_MAX_K &&
+          N * K <= kMaxElems))
+        return TL_ERR_SHAPE;
+    if (!aligned16(w) || !aligned16(signs) || !aligned16(codes) || !aligned16(scales))
+        return TL_ERR_ALIGN;
+    const int64_t wb = N * K * 4, cb = N * K, sb = N * (K / TL_GROUP) * 2;
+    if (overlap(codes, cb, w, wb) || overlap(codes, cb, signs, K) || overlap(codes, cb, scales, sb) ||
+        overlap(scales, sb, w, wb) || overlap(scales, sb, signs, K))
+        return TL_ERR_ALIAS;
+    return launched(tl::launch_quantize(w, signs, N, K, codes, scales, stream));
+}
+
 const char* tl_status_str(tl_status status) {
     switch (status) {
         case TL_OK: return "TL_OK";

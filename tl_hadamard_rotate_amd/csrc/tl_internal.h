@@ -58,6 +58,9 @@ bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
+// Rotate real-valued weight rows and round them to ternary g128
+hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
+                           int8_t* codes, uint16_t* scales, hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, hipStream_t stream);
