@@ -373,6 +373,20 @@ def quantize_weights(w: np.ndarray, signs: np.ndarray, block: int = BLOCK,
 
 
 # ---------------------------------------------------------------------------
+# bfloat16 activations (the bf16 variant of the product)
+# ---------------------------------------------------------------------------
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 number (8 significant bits, ties to the
+    even significand), returned as fp64 values.  For the bf16 variant of the
+    product (codes exact as bf16 -1/0/+1, the binary16 group scale applied in
+    fp32 afterwards); normal range only (|x| >= 2**-126), which activations
+    never leave."""
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))   # x = m * 2**e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+# ---------------------------------------------------------------------------
 # Error metrics
 # ---------------------------------------------------------------------------
 

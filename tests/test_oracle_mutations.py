@@ -11,7 +11,7 @@ from tests import test_oracle_pins as pins
 _orig = {name: getattr(ref, name) for name in
          ("hadamard", "rotate", "dequant", "matvec", "pack_trit5", "unpack_trit5",
           "pack_slot2", "unpack_slot2", "pack_bit1", "unpack_bit1", "quantize_ternary",
-          "fold_weights")}
+          "fold_weights", "round_bf16")}
 
 
 def _rotate_signs_last(x, signs, block=ref.BLOCK):
@@ -126,6 +126,21 @@ def _quantize_weights_unrotated(w, signs, block=ref.BLOCK, group=ref.GROUP):
     return ref.quantize_ternary(np.asarray(w, dtype=np.float64), group)
 
 
+def _round_bf16_truncate(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.trunc(m * 256.0), e - 8)
+
+
+def _round_bf16_half_up(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.floor(m * 256.0 + 0.5), e - 8)
+
+
+def _round_bf16_7_bits(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.rint(m * 128.0), e - 7)
+
+
 def _fold_weights_unsigned(w, signs, block=ref.BLOCK):
     return _orig["rotate"](w, np.ones_like(np.asarray(signs)), block)
 
@@ -151,6 +166,9 @@ MUTATIONS = {
                                      _quantize_with(_mean_scale, to_half=False)),
     "quantize_weights: rotation skipped": ("quantize_weights", _quantize_weights_unrotated),
     "fold_weights: signs dropped": ("fold_weights", _fold_weights_unsigned),
+    "round_bf16: truncation": ("round_bf16", _round_bf16_truncate),
+    "round_bf16: ties upward": ("round_bf16", _round_bf16_half_up),
+    "round_bf16: one significant bit short": ("round_bf16", _round_bf16_7_bits),
 }
 
 PIN_TESTS = [
@@ -175,6 +193,9 @@ PIN_TESTS = [
     (pins.test_quantize_scale_is_nearest_binary16_to_exact_mean_and_codes_nearest, {}),
     (pins.test_quantize_invariances, {}),
     (pins.test_quantize_weights_one_hot_closed_form, {}),
+    (pins.test_round_bf16_hand_worked, {}),
+    (pins.test_round_bf16_matches_bit_rounding_of_fp32, {}),
+    (pins.test_round_bf16_fixed_points_and_bound, {}),
 ]
 
 

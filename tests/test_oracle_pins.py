@@ -589,3 +589,52 @@ def test_quantize_weights_one_hot_closed_form():
         want_s = np.zeros(k_total // 128)
         want_s[8 * b:8 * (b + 1)] = 1.0 / 32
         assert np.array_equal(scales[r].astype(np.float64), want_s), k
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding of activations
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_hand_worked():
+    """bf16 keeps 8 significant bits: spacing 2^-7 in [1, 2)."""
+    cases = [
+        (1.0, 1.0),
+        (1.0 + 2.0 ** -8, 1.0),                       # tie, even significand 1.0000000
+        (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),       # tie between 1+2^-7 and 1+2^-6 -> even
+        (1.0 + 2.0 ** -8 + 2.0 ** -20, 1.0 + 2.0 ** -7),   # just above the tie
+        (-1.5, -1.5),
+        (3.0 + 2.0 ** -7, 3.0),                       # spacing 2^-6 in [2, 4): a tie -> even
+        (3.0 + 2.0 ** -6, 3.0 + 2.0 ** -6),           # representable
+        (255.5, 256.0),                               # spacing 1 in [128, 256): tie -> 256
+        (2.0 - 2.0 ** -9, 2.0),                       # rounds up into the next binade
+        (0.1, 0.10009765625),                         # 0.1 * 2^4 = 1.6 -> 205/128 * 2^-4
+    ]
+    for x, want in cases:
+        assert oracle.round_bf16(np.array([x]))[0] == want, x
+
+
+def _bf16_bits_rne(x32):
+    """Independent route: round the fp32 bit pattern to its top 16 bits,
+    nearest with ties to even."""
+    b = x32.view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def test_round_bf16_matches_bit_rounding_of_fp32():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # include exact ties of fp32 patterns: low 16 bits 0x8000
+    t = (rng.integers(0, 2 ** 31, 20000, dtype=np.uint64) & ~np.uint64(0xFFFF)) | np.uint64(0x8000)
+    x = np.concatenate([x, t.astype(np.uint32).view(np.float32)])
+    x = x[np.isfinite(x) & (np.abs(x) >= 2.0 ** -120) & (np.abs(x) < 2.0 ** 120)]
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), _bf16_bits_rne(x))
+
+
+def test_round_bf16_fixed_points_and_bound():
+    rng = np.random.default_rng(18)
+    x = rng.standard_normal(10000) * 10.0 ** rng.uniform(-6, 6, 10000)
+    r = oracle.round_bf16(x)
+    assert np.array_equal(oracle.round_bf16(r), r)                 # bf16 values stay put
+    assert np.all(np.abs(r - x) <= 2.0 ** -8 * np.abs(x))          # half spacing bound
+    assert np.all(np.diff(oracle.round_bf16(np.sort(x))) >= 0)     # monotone
