@@ -20,7 +20,8 @@ HIP events on the launch stream.  HBM traffic comes from the rocprofv3
 counter summary under profiles/ and is reported only while the kernel source
 is the one those counters were taken from.
 
-Extras: the other packing, the prefill GEMM sweep, batched decode over the
+Extras: the other packing, the prefill GEMM sweep (and its bfloat16 variant
+at M = 4096), batched decode over the
 attention projections, the rotation at prefill size, the 64-layer weight
 stream (one rotation per linear, and one per input with q|k|v and gate|up
 concatenated), the weight quantiser, the decode step with 1-bit weights, and
@@ -207,22 +208,25 @@ def _event_time(torch, fn, reps):
     return a.elapsed_time(b) / reps
 
 
-def bench_gemm(torch, tl, synth, dev, fmt, reps=5):
+def bench_gemm(torch, tl, synth, dev, fmt, reps=5, bf16=False, ms_list=None):
     """Prefill GEMM TFLOP/s for M in {512, 2048, 4096} at the MLP shapes
-    (gate: K=5120 N=17408, down: K=17408 N=5120)."""
+    (gate: K=5120 N=17408, down: K=17408 N=5120); with bf16, tl_gemm_bf16 on
+    bfloat16 activations (bfloat16 matrix peak = the fp16 one)."""
     out = []
+    call = tl.gemm_bf16 if bf16 else tl.gemm
+    xdt = torch.bfloat16 if bf16 else torch.float16
     for name in ("gate", "down"):
         k, n = synth.SHAPES[name]
         inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=synth.LINEAR_ID[name])
         packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
         scales = torch.from_numpy(inp.scales).to(dev)
-        for m in synth.PREFILL_M:
+        for m in ms_list or synth.PREFILL_M:
             gen = torch.Generator(device="cpu").manual_seed(4 + m)
-            x = torch.randn((m, k), generator=gen).to(torch.float16).to(dev)
+            x = torch.randn((m, k), generator=gen).to(xdt).to(dev)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
-            tl.gemm(packed, scales, fmt, x, out=y)
+            call(packed, scales, fmt, x, out=y)
             torch.cuda.synchronize()
-            ms = _event_time(torch, lambda i: tl.gemm(packed, scales, fmt, x, out=y), reps)
+            ms = _event_time(torch, lambda i: call(packed, scales, fmt, x, out=y), reps)
             tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             out.append({"linear": name, "M": m, "K": k, "N": n, "ms": round(ms, 4),
                         "TFLOPs": round(tflops, 2),
@@ -405,8 +409,9 @@ def bench_stream_shared(torch, tl, synth, dev, fmt, stream, reps=5):
 def bench_bit1(torch, tl, synth, dev, stream, copies, steps, warmup):
     """The decode step with 1-bit weights (codes -1/+1, g128 scales): per
     projection the rotation + the 1-bit GEMV (tl_linear, two launches), the
-    GEMV alone on rotated activations, and the GEMV at M = 1, 4, 16 on gate;
-    weights cycled over `copies` buffers, launches captured in HIP graphs."""
+    GEMV alone on rotated activations, and the GEMV at M = 1, 4, 16 on gate
+    (one graph of `copies` launches, one per weight copy); weights cycled
+    over `copies` buffers, launches captured in HIP graphs."""
     fmt = 2
     lins = build_step_inputs(torch, tl, synth, dev, fmt, copies)
     with torch.cuda.stream(stream):
@@ -427,11 +432,12 @@ def bench_bit1(torch, tl, synth, dev, stream, copies, steps, warmup):
         xm = torch.randn((m, k), generator=torch.Generator(device="cpu").manual_seed(m)).to(
             torch.float16).to(dev)
         ym = torch.empty((m, n), dtype=torch.float32, device=dev)
+        # all weight copies in one graph: launch time per GEMV, gaps included
         with torch.cuda.stream(stream):
-            gm = capture(torch, lambda c: tl.gemv(gate["packs"][c], gate["scales"][c], fmt, xm,
-                                                  out=ym), copies, stream)
-        r = max(steps, copies)
-        us = timed_replays(torch, gm, r, warmup, stream) * 1e3 / r
+            gm = capture(torch, lambda c: [tl.gemv(gate["packs"][i], gate["scales"][i], fmt, xm,
+                                                   out=ym) for i in range(copies)], 1, stream)
+        r = max(steps // copies, 3)
+        us = timed_replays(torch, gm, r, warmup, stream) * 1e3 / (r * copies)
         out["gate_batched"].append({"M": m, "us": round(us, 3),
                                     "GBs": round(gemv_bytes(n, k, m, fmt) / (us * 1e-6) / 1e9, 1)})
         del gm
@@ -619,6 +625,9 @@ def main(argv=None) -> int:
         torch.cuda.empty_cache()
         log("prefill GEMM (M = 512, 2048, 4096)")
         extra["gemm_prefill"] = bench_gemm(torch, tl, synth, dev, fmt)
+        log("prefill GEMM with bfloat16 activations (M = 4096)")
+        extra["gemm_prefill_bf16"] = bench_gemm(torch, tl, synth, dev, fmt, bf16=True,
+                                                ms_list=(4096,))
         log("batched decode GEMV over q, k, v, o (M = 1..16)")
         extra["batched_decode"] = bench_batched(torch, tl, synth, dev, fmt)
         log("rotation at prefill size")

@@ -167,6 +167,19 @@ TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_
                     const uint16_t* x, const int8_t* signs, int64_t M, int64_t N, int64_t K,
                     uint16_t* x_rot, void* y, int32_t y_dtype, hipStream_t stream);
 
+/* The prefill product with bfloat16 rotated activations:
+ *   y[m, n] = sum_g S[n, g] * sum_{k in g} code[n, k] * x_rot[m, k]
+ * with the codes entering the matrix cores as exact bfloat16 -1/0/+1 and each
+ * group's fp32 sum multiplied by its binary16 scale in fp32 (the scale is not
+ * rounded to bfloat16).  x_rot: bfloat16 [M, K] passed as uint16 bits; every
+ * other argument, rule and error as tl_gemm (the same workspace for dense
+ * trits and 1-bit codes, which are rewritten as 2-bit slots first).  For
+ * models whose activations are bfloat16; the binary16 tl_gemm is the more
+ * accurate product (bfloat16 keeps 8 significant bits against 11). */
+TL_API tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                              const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
+                              int32_t y_dtype, hipStream_t stream);
+
 /* Quantise real-valued weight rows to ternary g128, the rotation folded in
  * (page "OpenBonsai", section "How it works", steps 1 and 2: rotate with the
  * signed Hadamard transform, then round to -1, 0, +1 with one scale per 128;

@@ -151,3 +151,13 @@ def test_quantize_validation():
     assert call(codes=G - 16) == 5                 # over the signs
     assert call(scales=C + 4096 - 16) == 5         # scales over the codes (4 KB)
     assert call(scales=W) == 5
+
+
+def test_gemm_bf16_validation():
+    fn = tl.lib().tl_gemm_bf16
+    assert _gemv(fn, packed=NULL) == 1
+    assert _gemv(fn, k=1000) == 2
+    assert _gemv(fn, fmt=7) == 3
+    assert _gemv(fn, x=A + 2) == 4
+    assert _gemv(fn, y=A + 0x2000000) == 5
+    assert _gemv(fn, yd=3) == 7

@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
             "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p]),
             "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
+            "tl_gemm_bf16": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }
@@ -160,10 +161,10 @@ def quantize(w: torch.Tensor, signs: torch.Tensor):
     return codes, scales
 
 
-def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out):
+def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch.float16):
     _need(packed, "packed", torch.uint8, 2)
     _need(scales, "scales", torch.float16, 2)
-    _need(x_rot, "x_rot", torch.float16, 2)
+    _need(x_rot, "x_rot", x_dtype, 2)
     m, k = x_rot.shape
     n = packed.shape[0]
     if scales.shape != (n, k // GROUP):
@@ -188,6 +189,13 @@ def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out):
 def gemv(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
     """y[M, N] = x_rot . dequant(codes, scales)^T, decode-shaped (M <= 16)."""
     return _linear("tl_gemv", packed, scales, fmt, x_rot, out_dtype, out)
+
+
+def gemm_bf16(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """The prefill product with bfloat16 rotated activations x_rot [M, K]:
+    codes as bfloat16 -1/0/+1 on the matrix cores, group scales in fp32."""
+    return _linear("tl_gemm_bf16", packed, scales, fmt, x_rot, out_dtype, out,
+                   x_dtype=torch.bfloat16)
 
 
 def gemm(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:

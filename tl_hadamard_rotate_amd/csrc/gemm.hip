@@ -30,6 +30,7 @@ namespace tl {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -69,12 +70,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// digit -> bits of (d - 1) as binary16 (or bfloat16); an invalid digit decodes to 0
+template <bool BF16>
 __device__ __forceinline__ uint32_t code_bits(uint32_t d) {
-    // digit -> binary16 bits of (d - 1); an invalid digit decodes to 0
+    if (BF16) return d == 0u ? 0xBF80u : (d == 2u ? 0x3F80u : 0u);
     return d == 0u ? 0xBC00u : (d == 2u ? 0x3C00u : 0u);
 }
 
-template <int FMT>
+template <int FMT, bool BF16>
 __device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
     for (int c = tid; c < lut_bytes<FMT>() / 16; c += kThreads) {
         if (FMT == 0) {
@@ -84,7 +87,7 @@ __device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
                 uint32_t r = v;
 #pragma unroll
                 for (int i = 0; i < 5; ++i) {
-                    h[i] = code_bits(r % 3u);
+                    h[i] = code_bits<BF16>(r % 3u);
                     r /= 3u;
                 }
             }
@@ -92,8 +95,9 @@ __device__ __forceinline__ void build_lut(uint8_t* lut, int tid) {
                 uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
         } else {
             const uint32_t v = uint32_t(c) / (copies<FMT>() / 2);   // two 8-byte copies per piece
-            const uint32_t lo = code_bits(v & 3u) | (code_bits((v >> 2) & 3u) << 16);
-            const uint32_t hi = code_bits((v >> 4) & 3u) | (code_bits((v >> 6) & 3u) << 16);
+            const uint32_t lo = code_bits<BF16>(v & 3u) | (code_bits<BF16>((v >> 2) & 3u) << 16);
+            const uint32_t hi =
+                code_bits<BF16>((v >> 4) & 3u) | (code_bits<BF16>((v >> 6) & 3u) << 16);
             reinterpret_cast<uint4*>(lut)[c] = uint4{lo, hi, lo, hi};
         }
     }
@@ -170,7 +174,9 @@ __device__ __forceinline__ void decode_t5(const BRaw& r, uint32_t rep, half2v s2
     }
 }
 
-template <int FMT>
+// BF16: the codes as bfloat16 -1/0/+1, unscaled (the scale is applied to the
+// fp32 sums of each group); otherwise code * S in binary16
+template <int FMT, bool BF16>
 __device__ __forceinline__ void decode_b(const BRaw& r, int t, int hh, uint32_t rep,
                                          uint32_t (&out)[16]) {
     const uint16_t sh = uint16_t(r.s >> (16 * ((t >> 1) & 1)));   // wave-uniform select
@@ -180,8 +186,8 @@ __device__ __forceinline__ void decode_b(const BRaw& r, int t, int hh, uint32_t 
         for (int i = 0; i < 8; ++i) {
             const uint2 e = __builtin_bit_cast(
                 uint2, *reinterpret_cast<lds_u32x2*>(lut_off<1>(r.d[i >> 2], 8 * (i & 3), rep)));
-            out[2 * i] = scale_pair(e.x, s2);
-            out[2 * i + 1] = scale_pair(e.y, s2);
+            out[2 * i] = BF16 ? e.x : scale_pair(e.x, s2);
+            out[2 * i + 1] = BF16 ? e.y : scale_pair(e.y, s2);
         }
     } else {
         // wave-uniform: which 32 codes of the group, and the group's byte offset
@@ -206,7 +212,15 @@ struct ARaw {
     uint4 v[2];
 };
 
-template <int FMT>
+// BF16: x is bfloat16, the codes enter the matrix cores as bfloat16 -1/0/+1
+// and each group's fp32 sums are multiplied by their column's scale (the
+// K step of 64 is half a group, so every MFMA sums within one group).  The
+// group's sums need a second set of accumulators, so the tile is 64 x 256
+// (a wave owns 32 x 64) to stay within 256 registers.
+template <bool BF16>
+constexpr int tile_m() { return BF16 ? 64 : BM; }
+
+template <int FMT, bool BF16>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m, int64_t n,
     int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int chunk) {
@@ -217,7 +231,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     // XCD-aware tile order: XCD (blockIdx % 8) takes tiles [xcd * chunk, ...)
     const int tile = int(blockIdx.x & 7) * chunk + int(blockIdx.x >> 3);
     if (tile >= tiles) return;
-    const int64_t m0 = int64_t(tile / tiles_n) * BM;
+    constexpr int kBM = tile_m<BF16>(), kMI = kBM / 32;   // kMI: 16-row MFMA tiles per wave
+    const int64_t m0 = int64_t(tile / tiles_n) * kBM;
     const int64_t n0 = int64_t(tile % tiles_n) * BN;
 
     const int tid = threadIdx.x;
@@ -237,23 +252,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     const uint32_t rep = lds0 + uint32_t(lane & (copies<FMT>() - 1)) * uint32_t(entry_bytes<FMT>());
 
     // activation row and chunks of this thread
-    const int ar = tid >> 2, ac = 2 * (tid & 3);
+    // (BF16: one chunk per thread over 64 rows, else two over 128 rows)
+    constexpr int kAChunks = kBM / 64;
+    const int ar = tid / (8 / kAChunks), ac = kAChunks * (tid % (8 / kAChunks));
     const int64_t gm = m0 + ar < m ? m0 + ar : m - 1;          // rows past M copy row M-1
     const uint16_t* asrc = x + gm * k + 8 * ac;
 
     auto load_a = [&](ARaw& a, int t) {
         const uint4* p = reinterpret_cast<const uint4*>(asrc + BK * t);
-        a.v[0] = p[0];
-        a.v[1] = p[1];
+#pragma unroll
+        for (int c = 0; c < kAChunks; ++c) a.v[c] = p[c];
     };
     auto store_a = [&](const ARaw& a, int s) {
         const uint32_t base = st0 + uint32_t(s) * kStage;
-        *reinterpret_cast<lds_u32x4*>(base + swz(ar, ac)) = __builtin_bit_cast(u32x4, a.v[0]);
-        *reinterpret_cast<lds_u32x4*>(base + swz(ar, ac + 1)) = __builtin_bit_cast(u32x4, a.v[1]);
+#pragma unroll
+        for (int c = 0; c < kAChunks; ++c)
+            *reinterpret_cast<lds_u32x4*>(base + swz(ar, ac + c)) = __builtin_bit_cast(u32x4, a.v[c]);
     };
     auto store_b = [&](const BRaw& r, int t, int s) {
         uint32_t v[16];
-        decode_b<FMT>(r, t, hh, rep, v);
+        decode_b<FMT, BF16>(r, t, hh, rep, v);
         const uint32_t base = st0 + uint32_t(s) * kStage + kAStage;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -274,7 +292,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
         load_a(ra[i], i);
         load_b<FMT>(rb[i], prow, srow, i);
     }
-    build_lut<FMT>(smem, tid);
+    build_lut<FMT, BF16>(smem, tid);
     lds_barrier();   // the decode table
     store_a(ra[0], 0);
     store_b(rb[0], 0, 0);
@@ -282,36 +300,73 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
     load_b<FMT>(rb[0], prow, srow, 4);
     lds_barrier();
 
-    const int wm = (wave >> 2) * 64, wn = (wave & 3) * 64;
-    float4v acc[4][4];
+    const int wm = (wave >> 2) * (kBM / 2), wn = (wave & 3) * 64;
+    float4v acc[kMI][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = float4v{0.f, 0.f, 0.f, 0.f};
+    // BF16: this group's sums, and the scales of this lane's four output
+    // columns for the current group (loaded at the group's first step)
+    float4v grp[BF16 ? kMI : 1][BF16 ? 4 : 1];
+    uint32_t gsc[4] = {0, 0, 0, 0};
+    const uint16_t* scol[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t c = n0 + wn + 16 * j + (lane & 15);
+        scol[j] = scales + (c < n ? c : n - 1) * groups;   // columns past N read column N-1
+    }
 
     // one K step: MFMAs on stage t & 1, then step t + 1 (ring slot SLOT) to
-    // the other stage and step t + 5 loaded into that slot
+    // the other stage and step t + 5 loaded into that slot.  t is even for
+    // SLOT 1 and 3 (a group's first step) and odd for SLOT 2 and 0.
     auto step = [&](int t, auto slot_c) {
         constexpr int SLOT = decltype(slot_c)::value;
+        constexpr bool kFirst = SLOT == 1 || SLOT == 3;
         const int s = t & 1;
         const uint32_t a_base = st0 + uint32_t(s) * kStage;
         const uint32_t b_base = a_base + kAStage;
+        if (BF16 && kFirst) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gsc[j] = scol[j][t >> 1];
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             const int c = 4 * ks + (lane >> 4);
-            half8 af[4], bf[4];
+            u32x4 af[kMI], bf[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                af[i] = __builtin_bit_cast(
-                    half8, *reinterpret_cast<lds_u32x4*>(a_base + swz(wm + 16 * i + (lane & 15), c)));
-                bf[i] = __builtin_bit_cast(
-                    half8, *reinterpret_cast<lds_u32x4*>(b_base + swz(wn + 16 * i + (lane & 15), c)));
+            for (int i = 0; i < kMI; ++i)
+                af[i] = *reinterpret_cast<lds_u32x4*>(a_base + swz(wm + 16 * i + (lane & 15), c));
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                bf[j] = *reinterpret_cast<lds_u32x4*>(b_base + swz(wn + 16 * j + (lane & 15), c));
+#pragma unroll
+            for (int i = 0; i < kMI; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (BF16) {
+                        const float4v c0 = kFirst && ks == 0 ? float4v{0.f, 0.f, 0.f, 0.f}
+                                                             : grp[i][j];
+                        grp[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bf[j]),
+                            c0, 0, 0, 0);
+                    } else {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                            __builtin_bit_cast(half8, af[i]), __builtin_bit_cast(half8, bf[j]),
+                            acc[i][j], 0, 0, 0);
+                    }
+                }
+        }
+        if constexpr (BF16 && !kFirst) {
+            // the group is complete: y += S[column, group] * its sums, in fp32
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sj = float(__builtin_bit_cast(_Float16, uint16_t(gsc[j])));
+#pragma unroll
+                for (int i = 0; i < kMI; ++i)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(sj, grp[i][j][r], acc[i][j][r]);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
         // after the last step this writes a stage nobody reads
         const int t1 = t + 1 < ksteps ? t + 1 : ksteps - 1;
@@ -335,7 +390,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
 
     // lane holds D[4 * (lane / 16) + r][lane % 16] of each 16 x 16 tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kMI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -352,21 +407,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(
             }
 }
 
-template <int FMT>
+template <int FMT, bool BF16 = false>
 hipError_t launch(const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m,
                   int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<FMT>),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_kernel<FMT, BF16>),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  lds_bytes<FMT>());
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
+    const int64_t tiles_m = (m + tile_m<BF16>() - 1) / tile_m<BF16>(), tiles_n = (n + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t chunk = (tiles + 7) / 8;
-    hipLaunchKernelGGL(gemm_kernel<FMT>, dim3(unsigned(8 * chunk)), dim3(kThreads),
+    hipLaunchKernelGGL((gemm_kernel<FMT, BF16>), dim3(unsigned(8 * chunk)), dim3(kThreads),
                        size_t(lds_bytes<FMT>()), stream, packed, scales, x, m, n, k, y, y_f16,
                        int(tiles_n), int(tiles), int(chunk));
     return hipGetLastError();
@@ -402,6 +457,24 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt, c
     }
     return fmt == 0 ? launch<0>(packed, scales, x, m, n, k, y, y_f16, stream)
                     : launch<1>(packed, scales, x, m, n, k, y, y_f16, stream);
+}
+
+hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
+                            const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                            hipStream_t stream) {
+    if (m < 1 || n < 1 || k < 1024 || k % 1024 != 0) return hipErrorInvalidValue;
+    const uint8_t* s2 = packed;
+    if (fmt != 1) {
+        // dense trits and 1-bit codes: rewritten as 2-bit slots once per call
+        void* ws = nullptr;
+        hipError_t e = workspace(kWorkspaceSlot2, stream, size_t(n) * size_t(k / 4), &ws);
+        if (e != hipSuccess) return e;
+        e = fmt == 0 ? launch_trit5_to_slot2(packed, n, k, static_cast<uint8_t*>(ws), stream)
+                     : launch_bit1_to_slot2(packed, n, k, static_cast<uint8_t*>(ws), stream);
+        if (e != hipSuccess) return e;
+        s2 = static_cast<const uint8_t*>(ws);
+    }
+    return launch<1, true>(s2, scales, x, m, n, k, y, y_f16, stream);
 }
 
 }  // namespace tl

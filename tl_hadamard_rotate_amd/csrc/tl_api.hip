@@ -126,6 +126,15 @@ tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, co
         tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
 }
 
+tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                       const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
+                       int32_t y_dtype, hipStream_t stream) {
+    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    return launched(
+        tl::launch_gemm_bf16(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
+}
+
 tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x,
                     const int8_t* signs, int64_t M, int64_t N, int64_t K, uint16_t* x_rot, void* y,
                     int32_t y_dtype, hipStream_t stream) {

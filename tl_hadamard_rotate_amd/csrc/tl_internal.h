@@ -61,6 +61,11 @@ hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, cons
 // Rotate real-valued weight rows and round them to ternary g128
 hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
                            int8_t* codes, uint16_t* scales, hipStream_t stream);
+// The product with bfloat16 activations: codes as bfloat16 -1/0/+1 on the
+// matrix cores, each group's fp32 sums times the binary16 scale
+hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
+                            const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                            hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, hipStream_t stream);
