@@ -30,6 +30,7 @@ the CPU oracle on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
     python bench.py --profile-pass [--fmt slot2|trit5|bit1]
+    python bench.py --read-floor
 """
 from __future__ import annotations
 
@@ -471,6 +472,37 @@ def bench_quantize(torch, tl, synth, dev, reps=10):
     return out
 
 
+def read_floor(torch, tl, dev, reps=20) -> int:
+    """What HBM delivers to a read-only kernel (tl_stream_read) at transfer
+    sizes from 4 MiB to 512 MiB, including the 23.8 MB one gate/up decode
+    launch reads: buffers cycled through a 1 GiB pool, average time per
+    launch between HIP events (the rocprofv3 trace of this mode gives the
+    kernel durations).  Prints one JSON line."""
+    pool_bytes = 1 << 30
+    pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev).fill_(1)
+    out = torch.empty(65536, dtype=torch.int32, device=dev)
+    sizes = [4 << 20, 12 << 20, 23774208, 48 << 20, 96 << 20, 192 << 20, 512 << 20]
+    res = []
+    for b in sizes:
+        blocks = max(1024, min(65536, b // (256 * 16 * 4)))
+        slots = pool_bytes // b
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def call(i):
+            ptr = pool.data_ptr() + (i % slots) * b
+            st = tl.lib().tl_stream_read(ptr, b, out.data_ptr(), blocks, stream)
+            if st != 0:
+                raise RuntimeError(f"tl_stream_read failed: {st}")
+        call(0)
+        torch.cuda.synchronize()
+        ms = _event_time(torch, call, reps)
+        res.append({"bytes": b, "blocks": blocks, "us": round(ms * 1e3, 2),
+                    "GBs": round(b / (ms * 1e-3) / 1e9, 1)})
+        log(f"read {b / 2**20:7.1f} MiB: {ms * 1e3:8.2f} us, {b / (ms * 1e-3) / 1e9:7.1f} GB/s")
+    print(json.dumps({"read_floor": res}), flush=True)
+    return 0
+
+
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
     256 MiB written per launch), then 10 eager decode steps (per projection
@@ -541,6 +573,8 @@ def main(argv=None) -> int:
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs under rocprofv3: a 256 MiB device copy (the calibration "
                          "kernel, 3 launches) then 10 eager passes of the step's GEMVs; no timing")
+    ap.add_argument("--read-floor", action="store_true",
+                    help="time a read-only kernel at transfer sizes 4 MiB .. 512 MiB and exit")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="for counter runs under rocprofv3: the calibration copy, then the prefill "
                          "GEMM (M=4096, gate and down) and the rotation at M=4096; no timing")
@@ -567,6 +601,8 @@ def main(argv=None) -> int:
         return profile_pass(torch, tl, synth, dev, fmt)
     if args.profile_prefill:
         return profile_prefill(torch, tl, synth, dev)
+    if args.read_floor:
+        return read_floor(torch, tl, dev)
     log(f"building inputs fmt={args.fmt} copies={args.copies}")
     lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
     with torch.cuda.stream(stream):

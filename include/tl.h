@@ -198,6 +198,14 @@ TL_API tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int
                              int8_t* codes, uint16_t* scales, hipStream_t stream);
 
 /* Static name of a status code ("TL_OK", ...). */
+/* Measurement helper, not part of the layer: read `bytes` of device memory
+ * (16-byte aligned, a multiple of 16) with `blocks` workgroups of 256 threads
+ * (1..65536) and write one word per workgroup to out (uint32 [blocks], device,
+ * not overlapping buf).  Timing it gives what HBM delivers to a read-only
+ * kernel at that transfer size, the floor for the memory-bound kernels. */
+TL_API tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
+                                hipStream_t stream);
+
 TL_API const char* tl_status_str(tl_status status);
 
 /* Text of the last TL_ERR_LAUNCH on the calling thread ("" if none). */

@@ -161,3 +161,12 @@ def test_gemm_bf16_validation():
     assert _gemv(fn, x=A + 2) == 4
     assert _gemv(fn, y=A + 0x2000000) == 5
     assert _gemv(fn, yd=3) == 7
+
+
+def test_stream_read_validation():
+    f = tl.lib().tl_stream_read
+    assert f(NULL, 1024, A, 4, NULL) == 1
+    assert f(A, 1000, A + 0x100000, 4, NULL) == 2
+    assert f(A, 1024, A + 0x100000, 0, NULL) == 2
+    assert f(A + 8, 1024, A + 0x100000, 4, NULL) == 4
+    assert f(A, 1024, A + 16, 4, NULL) == 5

@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p]),
             "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
             "tl_gemm_bf16": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
+            "tl_stream_read": (i32, [p, i64, p, i32, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }

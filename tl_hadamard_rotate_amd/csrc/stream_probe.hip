@@ -1,0 +1,47 @@
+// Measurement helper, not part of the layer: a plain streaming read of a
+// device buffer (16-byte loads, grid-stride, four loads in flight per
+// thread), each workgroup writing one word so the loads stay.  It measures
+// what HBM delivers to a kernel that does nothing but read, at a given
+// transfer size: the floor a memory-bound kernel of that size can reach.
+#include "tl_internal.h"
+
+namespace tl {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __restrict__ p,
+                                                               int64_t n16,
+                                                               uint32_t* __restrict__ out) {
+    uint32_t acc = 0;
+    const int64_t stride = int64_t(gridDim.x) * kThreads;
+    int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = p[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t s;
+    if (threadIdx.x == 0) s = 0;
+    __syncthreads();
+    atomicXor(&s, acc);
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, int blocks,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(stream_read_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream,
+                       static_cast<const uint4*>(p), bytes / 16, out);
+    return hipGetLastError();
+}
+
+}  // namespace tl

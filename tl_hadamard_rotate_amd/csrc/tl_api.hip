@@ -174,6 +174,15 @@ tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int64_t K,
     return launched(tl::launch_quantize(w, signs, N, K, codes, scales, stream));
 }
 
+tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
+                         hipStream_t stream) {
+    if (!buf || !out) return TL_ERR_NULL;
+    if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return TL_ERR_SHAPE;
+    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(out) & 3u)) return TL_ERR_ALIGN;
+    if (overlap(out, int64_t(blocks) * 4, buf, bytes)) return TL_ERR_ALIAS;
+    return launched(tl::launch_stream_read(buf, bytes, out, blocks, stream));
+}
+
 const char* tl_status_str(tl_status status) {
     switch (status) {
         case TL_OK: return "TL_OK";

@@ -66,6 +66,9 @@ hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64
 hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
                             const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                             hipStream_t stream);
+// Measurement helper: streaming read of `bytes` (a multiple of 16) with `blocks` workgroups
+hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, int blocks,
+                              hipStream_t stream);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, hipStream_t stream);
