@@ -480,7 +480,7 @@ def read_floor(torch, tl, dev, reps=20) -> int:
     kernel durations).  Prints one JSON line."""
     pool_bytes = 1 << 30
     pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev).fill_(1)
-    out = torch.empty(65536, dtype=torch.int32, device=dev)
+    out = torch.full((65,), 0x5A5A5A5A, dtype=torch.int32, device=dev)   # out[0]: the key
     sizes = [4 << 20, 12 << 20, 23774208, 48 << 20, 96 << 20, 192 << 20, 512 << 20]
     res = []
     for b in sizes:

@@ -200,9 +200,10 @@ TL_API tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int
 /* Static name of a status code ("TL_OK", ...). */
 /* Measurement helper, not part of the layer: read `bytes` of device memory
  * (16-byte aligned, a multiple of 16) with `blocks` workgroups of 256 threads
- * (1..65536) and write one word per workgroup to out (uint32 [blocks], device,
- * not overlapping buf).  Timing it gives what HBM delivers to a read-only
- * kernel at that transfer size, the floor for the memory-bound kernels. */
+ * (1..65536).  out: uint32 [65] (device, not overlapping buf); out[0] is a
+ * key, and a lane whose xor of its words equals it writes out[1..64].
+ * Timing it gives what HBM delivers to a read-only kernel at that transfer
+ * size, the floor for the memory-bound kernels. */
 TL_API tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
                                 hipStream_t stream);
 

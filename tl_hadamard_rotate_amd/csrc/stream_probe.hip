@@ -1,8 +1,8 @@
 // Measurement helper, not part of the layer: a plain streaming read of a
 // device buffer (16-byte loads, grid-stride, four loads in flight per
-// thread), each workgroup writing one word so the loads stay.  It measures
-// what HBM delivers to a kernel that does nothing but read, at a given
-// transfer size: the floor a memory-bound kernel of that size can reach.
+// thread); a lane writes only if its xor matches a key, so the loads stay.
+// It measures what HBM delivers to a kernel that does nothing but read, at a
+// given transfer size: the floor a memory-bound kernel of that size can reach.
 #include "tl_internal.h"
 
 namespace tl {
@@ -27,12 +27,10 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const uint4* __re
         const uint4 v = p[i];
         acc ^= v.x ^ v.y ^ v.z ^ v.w;
     }
-    __shared__ uint32_t s;
-    if (threadIdx.x == 0) s = 0;
-    __syncthreads();
-    atomicXor(&s, acc);
-    __syncthreads();
-    if (threadIdx.x == 0) out[blockIdx.x] = s;
+    // the loads must stay: a lane stores only when its value matches the
+    // caller's key (no workgroup-wide reduction or barrier, which cost a
+    // read-only kernel several microseconds at these sizes)
+    if (acc == out[0]) out[1 + (blockIdx.x & 63)] = acc;
 }
 
 }  // namespace

@@ -179,7 +179,7 @@ tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t 
     if (!buf || !out) return TL_ERR_NULL;
     if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return TL_ERR_SHAPE;
     if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(out) & 3u)) return TL_ERR_ALIGN;
-    if (overlap(out, int64_t(blocks) * 4, buf, bytes)) return TL_ERR_ALIAS;
+    if (overlap(out, 65 * 4, buf, bytes)) return TL_ERR_ALIAS;
     return launched(tl::launch_stream_read(buf, bytes, out, blocks, stream));
 }
 
