@@ -83,9 +83,19 @@ def rotate_bytes(m: int, k: int) -> int:
 
 
 def source_sha(fmt: int) -> str:
-    path = os.path.join(ROOT, "tl_hadamard_rotate_amd", "csrc", KERNEL_SRC[fmt])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the SHA-256 of the kernel's source file followed
+    by the kernel headers it includes, in the order of its #include lines
+    (tl_internal.h, the library's declarations, is left out)."""
+    csrc = os.path.join(ROOT, "tl_hadamard_rotate_amd", "csrc")
+    with open(os.path.join(csrc, KERNEL_SRC[fmt]), "rb") as f:
+        data = f.read()
+    h = hashlib.sha256(data)
+    for name in re.findall(rb'^#include "([^"]+)"', data, re.M):
+        path = os.path.join(csrc, name.decode())
+        if name != b"tl_internal.h" and os.path.exists(path):
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(fmt: int):

@@ -155,10 +155,11 @@ TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t 
  * does); y as for tl_gemv.  Shape, format, dtype and alignment rules as
  * tl_gemv (x in place of x_rot); x_rot must not overlap x, signs, packed,
  * scales or y, and y must not overlap any input.  At M = 1 with
- * TL_FMT_SLOT2 (and K <= 20480) the rotation runs inside the GEMV kernel: one
- * launch, the rotated activations never make a round trip through memory
- * before use (x_rot is still written).  Otherwise: tl_hadamard_rotate, then
- * tl_gemv (M < 64) or tl_gemm (M >= 64).
+ * TL_FMT_SLOT2 (K <= 26624) or TL_FMT_TRIT5 (K <= 18432, and up to 22528 for
+ * most N) the rotation runs inside the GEMV kernel: one launch, the rotated
+ * activations never make a round trip through memory before use (x_rot is
+ * still written).  Otherwise: tl_hadamard_rotate, then tl_gemv (M < 64) or
+ * tl_gemm (M >= 64).
  * Linears that read the same input (q, k, v; gate, up) share its rotation:
  * the signs belong to the input, so their packed rows and scales can be
  * concatenated along N (row-major, so plain concatenation) and run as one

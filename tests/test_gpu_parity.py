@@ -301,8 +301,11 @@ def _rotation_bound_ok(got, want, x16):
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 1024), (1, 333, 5120), (1, 2048, 17408),
-                                   (3, 700, 2048), (70, 200, 3072)])
+                                   (1, 300, 24576), (3, 700, 2048), (70, 200, 3072)])
 def test_linear_matches_oracle(gpu, fmt, m, n, k):
+    """M = 1 runs the fused kernels (rotation in the GEMV's prologue) except
+    dense trits at K = 24576, whose rotation slots do not fit in LDS beside the
+    decode table: there the rotation and the GEMV are two launches."""
     inp = synth.linear_inputs(n, k, m, cfg=3, linear=m + n + k, outliers=True)
     packed = tl.pack(dev(inp.codes, gpu), fmt)
     scales = dev(inp.scales, gpu)
@@ -320,14 +323,15 @@ def test_linear_matches_oracle(gpu, fmt, m, n, k):
     assert oracle.rel_l2(y, oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)) < 2e-3
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
 @pytest.mark.parametrize("shape", ["gate", "down", "k"])
-def test_linear_full_size_sampled_rows(gpu, shape):
+def test_linear_full_size_sampled_rows(gpu, fmt, shape):
     """The fused M = 1 path at the 27B-class shapes; sampled rows against the
     oracle's layer, with the rotation folded into the weights."""
     k, n = synth.SHAPES[shape]
     inp = synth.linear_inputs(n, k, 1, cfg=5, linear=synth.LINEAR_ID[shape])
-    packed = tl.pack(dev(inp.codes, gpu), tl.FMT_SLOT2)
-    y = host(tl.linear(packed, dev(inp.scales, gpu), tl.FMT_SLOT2, dev(inp.x, gpu),
+    packed = tl.pack(dev(inp.codes, gpu), fmt)
+    y = host(tl.linear(packed, dev(inp.scales, gpu), fmt, dev(inp.x, gpu),
                        dev(inp.signs, gpu))).astype(np.float64)[0]
     rows = np.concatenate([np.random.default_rng(1).choice(n, size=200, replace=False), [0, n - 1]])
     want = oracle.linear(inp.x, inp.signs, inp.codes[rows], inp.scales[rows])[0]

@@ -37,14 +37,16 @@
 // groups; lanes l / 16 < 2 hold the first group, the others the second, and
 // v_permlane32_swap exchanges words so that each MFMA sees one group only.
 // Slots take contiguous runs of segments, block-major, so a slot's
-// activations change rarely.  Every weight load of a slot is issued before
-// the first wait; the per-lane activation images are built once per
-// workgroup in LDS while those loads are in flight.  Per-segment sums go to
-// LDS and are added in a fixed order (bitwise deterministic).
+// activations change rarely.  The first two steps' weight loads are in
+// flight while the per-lane activation images are built once per workgroup in
+// LDS; the rest of a slot's loads follow, all before its first wait on
+// weights.  Per-segment sums go to LDS and are added in a fixed order (bitwise
+// deterministic).
 #include <hip/hip_fp16.h>
 
 #include <type_traits>
 
+#include "rotate_lds.h"
 #include "tl_internal.h"
 
 namespace tl {
@@ -124,16 +126,14 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int nb, int t, uint4 (
     const int b = t >> 5;
     const int u = img_u(t);
     const int ep = img_ep(t);
-    if (t < nb * 32) {   // threads past the last block load nothing
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(x), 0, nb * 2048, kRsrcWord3);
+    const bool live = t < nb * 32;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + 1024 * b + eword_k(u, ep + 2 * h));
-            raw[2 * h] = src[0];
-            raw[2 * h + 1] = src[1];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) raw[i] = uint4{0, 0, 0, 0};
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t o = live ? uint32_t((1024 * b + eword_k(u, ep + 2 * h)) * 2) : kOob;
+        raw[2 * h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
+        raw[2 * h + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, live ? o + 16 : kOob, 0, 0));
     }
 }
 
@@ -199,80 +199,6 @@ __device__ void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t* img, u
         *reinterpret_cast<float4*>(rec + (b * 4 + (u >> 2)) * kRecBytes) =
             float4{pow2f(10 + ex), -sum * unit, -other * unit, 0.0f};
     }
-}
-
-// Fused rotation (tl_linear).  Half-wave hw (32 lanes) rotates block hw:
-// lane j loads elements [32j, 32j + 32) and their signs, does the butterflies
-// of index bits 0-4 in registers, transposes through LDS (row stride 33
-// floats: conflict-free both ways), does bits 5-9 in registers, and writes
-// (1/32) * result, rounded once to binary16, to the block's activations in
-// LDS.  fp32 throughout, 10 butterfly levels per output, like
-// tl_hadamard_rotate (summation order differs, so results agree to within
-// that bound rather than bit for bit).
-constexpr int kRotScratch = 32 * 33 * 4;   // bytes of transpose scratch per block
-
-__device__ __forceinline__ void rot_load(const uint16_t* x, const int8_t* signs, int nb, int t,
-                                         uint4 (&xr)[4], uint4 (&sr)[2]) {
-    const int hw = t >> 5, j = t & 31;
-    if (hw < nb) {
-        const uint4* px = reinterpret_cast<const uint4*>(x + 1024 * hw + 32 * j);
-        const uint4* ps = reinterpret_cast<const uint4*>(signs + 1024 * hw + 32 * j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = px[i];
-        sr[0] = ps[0];
-        sr[1] = ps[1];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xr[i] = uint4{0, 0, 0, 0};
-        sr[0] = sr[1] = uint4{0, 0, 0, 0};
-    }
-}
-
-template <int H>
-__device__ __forceinline__ void butterfly(float (&v)[32]) {
-#pragma unroll
-    for (int i = 0; i < 32; ++i)
-        if (!(i & H)) {
-            const float a = v[i], b = v[i + H];
-            v[i] = a + b;
-            v[i + H] = a - b;
-        }
-}
-
-__device__ __forceinline__ void butterflies(float (&v)[32]) {
-    butterfly<1>(v);
-    butterfly<2>(v);
-    butterfly<4>(v);
-    butterfly<8>(v);
-    butterfly<16>(v);
-}
-
-__device__ void rot_run(const uint4 (&xr)[4], const uint4 (&sr)[2], int nb, int t, float* scratch,
-                        uint16_t* xrot) {
-    const int hw = t >> 5, j = t & 31;
-    if (hw >= nb) return;   // whole half-waves
-    const uint32_t xw[16] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w, xr[1].x, xr[1].y, xr[1].z, xr[1].w,
-                             xr[2].x, xr[2].y, xr[2].z, xr[2].w, xr[3].x, xr[3].y, xr[3].z, xr[3].w};
-    const uint32_t sw[8] = {sr[0].x, sr[0].y, sr[0].z, sr[0].w, sr[1].x, sr[1].y, sr[1].z, sr[1].w};
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        // a negative sign byte flips the sign bit of the fp32 value
-        const uint32_t neg = ((sw[i >> 2] >> (8 * (i & 3) + 7)) & 1u) << 31;
-        v[i] = __builtin_bit_cast(float,
-                                  __builtin_bit_cast(uint32_t, h2f((xw[i >> 1] >> (16 * (i & 1))) & 0xFFFFu)) ^ neg);
-    }
-    butterflies(v);
-    float* row = scratch + hw * (32 * 33);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) row[j * 33 + i] = v[i];
-    // the same wave wrote the rows: its LDS operations complete in order
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = row[i * 33 + j];   // element 32 i + j
-    butterflies(v);
-    uint16_t* out = xrot + 1024 * hw + j;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) out[32 * i] = uint16_t(f2h(v[i] * 0.03125f));
 }
 
 // load_x from the rotated activations in LDS
@@ -460,11 +386,13 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     // activations, then the first two steps' weights, then the activation images
     // (built by the waves that hold activations), then the rest of the
     // weights.  Requested behind the whole weight stream, the activations
-    // would arrive microseconds later.
+    // would arrive microseconds later (and requesting every step before the
+    // images was measured slower).  The activation loads are branch-free
+    // buffer loads, so no wave waits for them before its weight loads go out.
     uint4 xraw[4];
     if constexpr (ROT) {
         uint4 sr[2];
-        rot_load(x, signs, nb, tid, xraw, sr);
+        rot::load(x, signs, nb, tid, xraw, sr);
         set_chunk(0);
         issue(0, Zero{}, Head{});
         // the empty asm keeps the rotation below those weight loads
@@ -477,7 +405,8 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
                      "+v"(sr[1].y), "+v"(sr[1].z), "+v"(sr[1].w)
                      :
                      : "memory");
-        rot_run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), xrot);   // nb <= 32 half-waves
+        rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
+                 kBlock);   // nb <= 32 half-waves
         lds_barrier();
         if (blockIdx.x == 0)
             for (int i = tid; i < nb * 128; i += kThreads)
@@ -563,8 +492,8 @@ M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     p.rpc = int(rpc);
     p.steps = int((rpc * nb + kSlots - 1) / kSlots);
     const size_t tail = size_t(nb) * kImgBlock + size_t(nb) * 4 * kRecBytes + size_t(rpc * nb) * 16;
-    p.lds = rot ? size_t(nb) * 2048 + (tail > size_t(nb) * kRotScratch ? tail : size_t(nb) * kRotScratch)
-                : tail;
+    const size_t scratch = size_t(nb) * rot::kScratchBytes;
+    p.lds = rot ? size_t(nb) * 2048 + (tail > scratch ? tail : scratch) : tail;
     return p;
 }
 

@@ -39,6 +39,7 @@
 // one v_perm_b32 with a constant selector.
 #include <hip/hip_fp16.h>
 
+#include "rotate_lds.h"
 #include "tl_internal.h"
 
 namespace tl {
@@ -235,30 +236,38 @@ __device__ __forceinline__ void compute_block(const Block& b, uint32_t rep, cons
     }
 }
 
+// xstride: bytes from one 1024-block of activations to the next
 template <int NR, int NT, bool XLDS>
 __device__ __forceinline__ void flight(const uint8_t* wb, const uint16_t* sb, uint32_t rep,
-                                       const XSrc<NT, XLDS>& xs, uint32_t off, float (&acc)[NT]) {
+                                       const XSrc<NT, XLDS>& xs, uint32_t off, uint32_t xstride,
+                                       float (&acc)[NT]) {
     Block b[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) load_block(b[i], wb + kBlockBytes * i, sb + 8 * i);
 #pragma unroll
-    for (int i = 0; i < NR; ++i) compute_block<NT, XLDS>(b[i], rep, xs, off + 2048u * i, acc);
+    for (int i = 0; i < NR; ++i) compute_block<NT, XLDS>(b[i], rep, xs, off + xstride * i, acc);
 }
 
 template <int NT, bool XLDS>
 __device__ __forceinline__ void flight_n(int nr, const uint8_t* wb, const uint16_t* sb,
                                          uint32_t rep, const XSrc<NT, XLDS>& xs, uint32_t off,
-                                         float (&acc)[NT]) {
+                                         uint32_t xstride, float (&acc)[NT]) {
     if (flight_max<NT>() >= 2 && nr >= 2)
-        flight<(flight_max<NT>() >= 2 ? 2 : 1), NT, XLDS>(wb, sb, rep, xs, off, acc);
+        flight<(flight_max<NT>() >= 2 ? 2 : 1), NT, XLDS>(wb, sb, rep, xs, off, xstride, acc);
     else if (nr >= 1)
-        flight<1, NT, XLDS>(wb, sb, rep, xs, off, acc);
+        flight<1, NT, XLDS>(wb, sb, rep, xs, off, xstride, acc);
 }
 
-template <int NT, bool XLDS>
+// ROT (M = 1, activations in LDS): x holds the unrotated activations and
+// signs their signs; the workgroup rotates them into LDS first, one
+// rot::kScratchBytes slot per 1024-block (the block's transpose scratch, then
+// its 1024 binary16 values), and workgroup 0 also writes them to x_rot.
+template <int NT, bool XLDS, bool ROT>
 __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
-    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int m, int64_t n, int64_t k,
-    int ksplit, int64_t rows_base, int64_t rows_rem, void* __restrict__ y, int y_f16) {
+    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, const int8_t* signs,
+    uint16_t* x_rot, int m, int64_t n, int64_t k, int ksplit, int64_t rows_base, int64_t rows_rem,
+    void* __restrict__ y, int y_f16) {
+    static_assert(!ROT || (NT == 1 && XLDS), "the rotating prologue is for one token in LDS");
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     uint8_t* lut = smem;                                             // LDS address 0
     const int nthreads = blockDim.x;
@@ -291,17 +300,36 @@ __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
     // published before any weight load is issued.
     const uint32_t xs_lds =
         uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t*)(xs)));
-    const uint32_t zero_lds = xs_lds + uint32_t(m) * uint32_t(k) * 2u;   // 16-byte zero pad
-    if (XLDS) {
-        const int pieces = int(int64_t(m) * k / 512);   // M*K is a multiple of 1024
-        for (int c = wave; c < pieces; c += nwaves)
-            dma_1k(xs_lds + uint32_t(c) * 1024u, x + int64_t(c) * 512 + lane * 8);
+    const uint32_t xstride = ROT ? uint32_t(rot::kScratchBytes) : 2048u;   // per 1024-block
+    const uint32_t zero_lds = xs_lds + uint32_t(m) * uint32_t(blocks) * xstride;   // 16-byte zero pad
+    if constexpr (ROT) {
+        // the loads go out first, the table is built while they are in flight
+        uint4 xr[4], sr[2];
+        rot::load(x, signs, blocks, tid, xr, sr);
+        build_lut(lut, tid, nthreads);
         if (tid == 0)
             *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(zero_lds) =
                 u32x4{0, 0, 0, 0};
+        rot::run(xr, sr, blocks, tid, reinterpret_cast<float*>(xs), rot::kScratchFloats, xs,
+                 rot::kScratchBytes / 2);   // blocks * 32 <= nthreads (checked on the host)
+        vm_lds_barrier();
+        if (blockIdx.x == 0)
+            for (int i = tid; i < blocks * 128; i += nthreads)
+                reinterpret_cast<uint4*>(x_rot)[i] = *reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const uint8_t*>(xs) + (i >> 7) * rot::kScratchBytes +
+                    (i & 127) * 16);
+    } else {
+        if (XLDS) {
+            const int pieces = int(int64_t(m) * k / 512);   // M*K is a multiple of 1024
+            for (int c = wave; c < pieces; c += nwaves)
+                dma_1k(xs_lds + uint32_t(c) * 1024u, x + int64_t(c) * 512 + lane * 8);
+            if (tid == 0)
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(zero_lds) =
+                    u32x4{0, 0, 0, 0};
+        }
+        build_lut(lut, tid, nthreads);
+        vm_lds_barrier();
     }
-    build_lut(lut, tid, nthreads);
-    vm_lds_barrier();
 
     const uint32_t rep = uint32_t(lane & 15) * 16u;   // this lane's table copy * 16
     // A-operand role: row j of A = token j / 4 of the pass, lane-group class j % 4
@@ -314,7 +342,9 @@ __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
         const bool live = (j & 3) == q && (4 * p + a_tok) < m;
         const int64_t xoff = int64_t(4 * p + a_tok) * k + kBlock * b0 + 256 * q;   // halves
         if constexpr (XLDS) {
-            xsrc.base[p] = live ? xs_lds + uint32_t(xoff) * 2u : zero_lds;
+            const uint32_t lds_off = (uint32_t(4 * p + a_tok) * uint32_t(blocks) + uint32_t(b0)) *
+                                         xstride + 512u * uint32_t(q);
+            xsrc.base[p] = live ? xs_lds + lds_off : zero_lds;
             xsrc.mask[p] = live ? ~0u : 0u;
         } else {
             xsrc.ptr[p] = reinterpret_cast<const uint8_t*>(x + (live ? xoff : 0));
@@ -334,7 +364,7 @@ __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
     for (;;) {   // tiles of this wave (a single one unless ksplit == 1)
         for (int f = 0; f < nb; f += kFlight)
             flight_n<NT, XLDS>(nb - f, wb + kBlockBytes * f, sb + 8 * f, rep, xsrc,
-                               2048u * uint32_t(f), acc);
+                               xstride * uint32_t(f), xstride, acc);
         tile += tile_stride;
         if (ksplit > 1 || tile >= tiles_here) break;
         // whole-K tiles: write this one out and start the next
@@ -417,25 +447,32 @@ Plan make_plan(int64_t n, int max_w) {
     return p;
 }
 
-template <int NT, bool XLDS>
+// LDS bytes of a launch: table, reduction buffer, activations (one rotation
+// slot per 1024-block when the kernel rotates) and a 16-byte zero pad
+template <int NT, bool XLDS, bool ROT>
+constexpr int64_t lds_bytes(int mt, int64_t k) {
+    return kLutBytes + int64_t(waves<NT>()) * NT * 64 * 4 +
+           (XLDS ? (ROT ? (k / kBlock) * rot::kScratchBytes : int64_t(mt) * k * 2) + 16 : 0);
+}
+
+template <int NT, bool XLDS, bool ROT = false>
 hipError_t launch_one(const Plan& plan, const uint8_t* packed, const uint16_t* scales,
-                      const uint16_t* x, int mt, int64_t n, int64_t k, void* y, int y_f16,
-                      hipStream_t stream) {
+                      const uint16_t* x, const int8_t* signs, uint16_t* x_rot, int mt, int64_t n,
+                      int64_t k, void* y, int y_f16, hipStream_t stream) {
     static bool attr_set = false;
     if (!attr_set) {
         const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemv_trit5_kernel<NT, XLDS>),
+            reinterpret_cast<const void*>(gemv_trit5_kernel<NT, XLDS, ROT>),
             hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsLimit));
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    size_t lds = size_t(kLutBytes) + size_t(waves<NT>()) * NT * 64 * 4 +
-                 (XLDS ? size_t(mt) * size_t(k) * 2 + 16 : 0);
+    size_t lds = size_t(lds_bytes<NT, XLDS, ROT>(mt, k));
     // ask for more than half of the CU's LDS so that two workgroups never share a CU
     if (lds < size_t(kLdsLimit / 2 + 1024)) lds = size_t(kLdsLimit / 2 + 1024);
-    hipLaunchKernelGGL((gemv_trit5_kernel<NT, XLDS>), dim3(unsigned(plan.grid)),
-                       dim3(64 * plan.waves), lds, stream, packed, scales, x, mt, n, k,
-                       plan.ksplit, n / plan.grid, n % plan.grid, y, y_f16);
+    hipLaunchKernelGGL((gemv_trit5_kernel<NT, XLDS, ROT>), dim3(unsigned(plan.grid)),
+                       dim3(64 * plan.waves), lds, stream, packed, scales, x, signs, x_rot, mt, n,
+                       k, plan.ksplit, n / plan.grid, n % plan.grid, y, y_f16);
     return hipGetLastError();
 }
 
@@ -447,11 +484,30 @@ hipError_t launch_nt(const uint8_t* packed, const uint16_t* scales, const uint16
     // table and the reduction buffer
     const int64_t budget = kLdsLimit - kLutBytes - int64_t(waves<NT>()) * NT * 64 * 4;
     if (int64_t(mt) * k * 2 + 16 <= budget)
-        return launch_one<NT, true>(plan, packed, scales, x, mt, n, k, y, y_f16, stream);
-    return launch_one<NT, false>(plan, packed, scales, x, mt, n, k, y, y_f16, stream);
+        return launch_one<NT, true>(plan, packed, scales, x, nullptr, nullptr, mt, n, k, y, y_f16,
+                                    stream);
+    return launch_one<NT, false>(plan, packed, scales, x, nullptr, nullptr, mt, n, k, y, y_f16,
+                                 stream);
 }
 
 }  // namespace
+
+// tl_linear at M = 1 in one launch: every 1024-block needs a half-wave of the
+// workgroup for its rotation, and its slot must fit in LDS beside the table
+bool linear_m1_trit5_fits(int64_t m, int64_t n, int64_t k) {
+    if (m != 1) return false;
+    const Plan plan = make_plan(n, waves<1>());
+    return (k / kBlock) * 32 <= int64_t(plan.waves) * 64 &&
+           lds_bytes<1, true, true>(1, k) <= kLdsLimit;
+}
+
+hipError_t launch_linear_m1_trit5(const uint8_t* packed, const uint16_t* scales,
+                                  const uint16_t* x, const int8_t* signs, uint16_t* x_rot,
+                                  int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    const Plan plan = make_plan(n, waves<1>());
+    return launch_one<1, true, true>(plan, packed, scales, x, signs, x_rot, 1, n, k, y, y_f16,
+                                     stream);
+}
 
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,

@@ -152,6 +152,9 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
     if (fmt == TL_FMT_SLOT2 && tl::linear_m1_slot2_fits(M, N, K))
         return launched(
             tl::launch_linear_m1_slot2(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
+    if (fmt == TL_FMT_TRIT5 && tl::linear_m1_trit5_fits(M, N, K))
+        return launched(
+            tl::launch_linear_m1_trit5(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
     hipError_t e = tl::launch_hadamard(x, signs, M, K, x_rot, stream);
     if (e != hipSuccess) return launched(e);
     e = M >= 64 ? tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream)

@@ -34,6 +34,12 @@ bool linear_m1_slot2_fits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                   const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
                                   void* y, int y_f16, hipStream_t stream);
+// Dense trits at M = 1 with the rotation fused in front (x unrotated; x_rot
+// receives the rotated activations); usable when linear_m1_trit5_fits
+bool linear_m1_trit5_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_linear_m1_trit5(const uint8_t* packed, const uint16_t* scales,
+                                  const uint16_t* x, const int8_t* signs, uint16_t* x_rot,
+                                  int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream);
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
