@@ -3,8 +3,8 @@
 A step is one decode pass (M = 1) over the 27B-class MLP projections
 gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120): for
 each projection the signed 1024-block Hadamard rotation of its input and the
-ternary product (tl_linear: one fused kernel per projection with the 2-bit-slot
-packing, rotation + GEMV kernels with the dense trit packing).  Inputs are
+ternary product (tl_linear: one fused kernel per projection with either
+packing).  Inputs are
 seeded synthetic tensors with the workload's distributions.
 
 Timing.  Each step is captured once in a HIP graph; the weights are replicated
@@ -14,9 +14,8 @@ W warm-up steps, then exactly K timed steps between two HIP events on the
 launch stream, with a device synchronisation on both sides.
 
 Dominant kernel (roofline): the fused tl_linear kernel, whose three launches
-make up the step (2-bit slots), or the GEMV timed on its own in a graph of
-three launches per weight copy (dense trits); average launch time between
-HIP events on the launch stream.  HBM traffic comes from the rocprofv3
+make up the step; average launch time between HIP events on the launch
+stream.  HBM traffic comes from the rocprofv3
 counter summary under profiles/ and is reported only while the kernel source
 is the one those counters were taken from.
 
@@ -101,7 +100,7 @@ def source_sha(fmt: int) -> str:
 def traffic_from_profiles(fmt: int):
     """HBM bytes per GEMV launch from the committed counter summary, or None
     when there is none for the current kernel source."""
-    name = "linear_m1_slot2" if fmt == 1 else "gemv_trit5"
+    name = "linear_m1_slot2" if fmt == 1 else "linear_m1_trit5"
     path = os.path.join(ROOT, "profiles", f"{name}_decode_mlp_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -135,7 +134,7 @@ def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
 
 def step_fn(tl, lins, fmt, c):
     """One decode step: per projection, rotation + ternary product (tl_linear;
-    a single fused kernel at M=1 with the 2-bit-slot packing)."""
+    a single fused kernel at M=1 with the 2-bit-slot and dense trit packings)."""
     for lin in lins:
         tl.linear(lin["packs"][c], lin["scales"][c], fmt, lin["x"], lin["signs"],
                   out=lin["y"], x_rot=lin["x_rot"])
@@ -628,15 +627,12 @@ def main(argv=None) -> int:
     g_ms = timed_replays(torch, gemv_graphs, reps, args.warmup, stream)
     g_us = g_ms * 1e3 / (3 * reps)
     g_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
-    # dominant kernel: with the 2-bit-slot packing the step is three launches
-    # of the fused rotate + GEMV kernel, so the step replays time it directly;
-    # otherwise it is the GEMV, timed alone
-    if fmt == 1:
-        avg_us = ms * 1e3 / 3.0
-        per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
-        kname = "tl_linear (gemv_m1_slot2_kernel, rotation fused)"
-    else:
-        avg_us, per_launch, kname = g_us, g_bytes, "tl_gemv (gemv_trit5_kernel)"
+    # dominant kernel: the step is three launches of the fused rotate + GEMV
+    # kernel, so the step replays time it directly
+    avg_us = ms * 1e3 / 3.0
+    per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+    kname = ("tl_linear (gemv_m1_slot2_kernel, rotation fused)" if fmt == 1 else
+             "tl_linear (gemv_trit5_kernel, rotation fused)")
     achieved = per_launch / (avg_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(fmt)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
