@@ -324,6 +324,30 @@ def test_linear_matches_oracle(gpu, fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
+@pytest.mark.parametrize("n,k", [(1, 1024), (17, 2048), (1, 18432), (4097, 1024)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16], ids=["f32", "f16"])
+def test_linear_fused_plan_edges(gpu, fmt, n, k, out_dtype):
+    """The fused M = 1 kernels at the edges of their launch plans: one row
+    (one workgroup whose waves split K), a ragged row tile, 18 blocks (the
+    largest K at which the dense-trit rotation slots fit for every N) and a
+    ragged last row slice; fp32 and binary16 outputs.  The product equals the
+    library's GEMV on the x_rot the call wrote, bit for bit, and the layer
+    meets the 2e-3 bar against the oracle."""
+    inp = synth.linear_inputs(n, k, 1, cfg=3, linear=n + k, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), fmt)
+    scales = dev(inp.scales, gpu)
+    x_rot = torch.empty((1, k), dtype=torch.float16, device=gpu)
+    y = host(tl.linear(packed, scales, fmt, dev(inp.x, gpu), dev(inp.signs, gpu),
+                       out_dtype=out_dtype, x_rot=x_rot))
+    assert _rotation_bound_ok(host(x_rot).astype(np.float64), oracle.rotate(inp.x, inp.signs), inp.x)
+    y2 = host(tl.gemv(packed, scales, fmt, x_rot, out_dtype=out_dtype))
+    assert np.array_equal(y.view(np.uint16 if out_dtype == torch.float16 else np.uint32),
+                          y2.view(np.uint16 if out_dtype == torch.float16 else np.uint32))
+    want = oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)
+    assert oracle.rel_l2(y.astype(np.float64), want) < 2e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
 @pytest.mark.parametrize("shape", ["gate", "down", "k"])
 def test_linear_full_size_sampled_rows(gpu, fmt, shape):
     """The fused M = 1 path at the 27B-class shapes; sampled rows against the

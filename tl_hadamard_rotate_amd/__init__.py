@@ -208,7 +208,7 @@ def linear(packed, scales, fmt, x, signs, out_dtype=torch.float32, out=None,
            x_rot=None) -> torch.Tensor:
     """y[M, N] = R(x) . dequant(codes, scales)^T on unrotated fp16 x [M, K];
     x_rot (allocated when None) receives R(x).  One fused launch at M = 1
-    with the 2-bit-slot packing."""
+    with the 2-bit-slot and dense trit packings (within their K limits)."""
     _need(packed, "packed", torch.uint8, 2)
     _need(scales, "scales", torch.float16, 2)
     _need(x, "x", torch.float16, 2)
