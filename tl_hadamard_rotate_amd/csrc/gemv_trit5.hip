@@ -107,19 +107,25 @@ __device__ __forceinline__ uint32_t code_bits(uint32_t d) {
 }
 
 __device__ __forceinline__ void build_lut(uint8_t* lut, int tid, int nthreads) {
-    // consecutive threads write consecutive 16-byte pieces (row v, copy c)
-    for (int c = tid; c < kLutBytes / 16; c += nthreads) {
-        const uint32_t v = uint32_t(c) >> 4;
+    // Thread t fills row v = t / 4: it decodes byte value v once and writes
+    // copies r, r + 4, r + 8 and r + 12 (r = t % 4), starting with copy
+    // (r + 4 v) % 16, so the 16 lanes that an LDS write serves together hit 16
+    // distinct 16-byte bank groups.
+    for (int t = tid; t < 1024; t += nthreads) {
+        const uint32_t v = uint32_t(t) >> 2, r = uint32_t(t) & 3u;
         uint32_t h[5] = {0, 0, 0, 0, 0};
         if (v < 243) {
-            uint32_t r = v;
+            uint32_t rem = v;
 #pragma unroll
             for (int i = 0; i < 5; ++i) {
-                h[i] = code_bits(r % 3u);
-                r /= 3u;
+                h[i] = code_bits(rem % 3u);
+                rem /= 3u;
             }
         }
-        reinterpret_cast<uint4*>(lut)[c] = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
+        const uint4 e = uint4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i)
+            reinterpret_cast<uint4*>(lut)[v * 16 + ((r + 4 * (v + i)) & 15u)] = e;
     }
 }
 
