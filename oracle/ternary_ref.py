@@ -24,7 +24,7 @@ What it computes (every step is the plain definition, no fast algorithm):
   about 1.125 bits per weight.  Source: page "How Prism ML Squeezed a 27B
   Model Into 3.9 GB" (dev.to), list "Two formats ship today".
 
-Readings taken where the pages are silent (all listed in the design doc):
+Readings taken where the pages are silent:
 
 * R(x)[1024 b + i] = (1/32) * sum_j H[i, j] * s[1024 b + j] * x[1024 b + j],
   H the Sylvester (natural order) Hadamard matrix, signs applied first.  The
@@ -41,8 +41,13 @@ Readings taken where the pages are silent (all listed in the design doc):
   S = binary16(mean |w'| over the group), c = clip(rint(w' / S), -1, 1)
   (ties to even, so |w'| = S/2 gives 0), c = 0 where S = 0.
 
-Parity status of every function here is recorded in the design doc; the pins live
-in tests/test_oracle_*.py.
+Every function here is pinned to something other than itself: hand-worked
+values, closed forms, brute force on tiny cases and invariants in
+tests/test_oracle_pins.py, and planted mistakes those pins must catch in
+tests/test_oracle_mutations.py.  Parity unpinned: byte compatibility of the
+packings with the published model files, whose layouts the pages do not give
+(the formats above are this library's own and are pinned to their own
+definition).
 """
 from __future__ import annotations
 
