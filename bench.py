@@ -29,6 +29,7 @@ the CPU oracle on a bounded sample.
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
     python bench.py --profile-pass [--fmt slot2|trit5|bit1]
+    python bench.py --profile-prefill | --profile-batched
     python bench.py --read-floor
 """
 from __future__ import annotations
@@ -569,6 +570,56 @@ def profile_prefill(torch, tl, synth, dev) -> int:
     return 0
 
 
+def profile_batched(torch, tl, synth, dev) -> int:
+    """Kernels for the batched-decode, quantiser and bf16-GEMM counter runs:
+    the calibration copy (3 launches of a 256 MiB device copy); then, for q
+    (K=5120, N=6144) and o (K=6144, N=5120) with 2-bit slots, at M = 2, 4, 8
+    and 16 in that order, 4 tl_gemv launches on rotated activations, one per
+    weight copy; then 3 launches of tl_quantize at the gate shape (N=17408,
+    K=5120); then 2 launches of tl_gemm_bf16 at M=4096 for gate."""
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for name in ("q", "o"):
+        k, n = synth.SHAPES[name]
+        inp = synth.linear_inputs(n, k, 16, seed=0, cfg=3, linear=synth.LINEAR_ID[name],
+                                  outliers=True)
+        packed = tl.pack(torch.from_numpy(inp.codes).to(dev), 1)
+        scales = torch.from_numpy(inp.scales).to(dev)
+        packs = [packed] + [packed.clone() for _ in range(3)]
+        scs = [scales] + [scales.clone() for _ in range(3)]
+        x_rot = tl.hadamard_rotate(torch.from_numpy(inp.x).to(dev),
+                                   torch.from_numpy(inp.signs).to(dev))
+        for m in (2, 4, 8, 16):
+            xm = x_rot[:m].contiguous()
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            for c in range(4):
+                tl.gemv(packs[c], scs[c], 1, xm, out=y)
+            torch.cuda.synchronize()
+        del packs, scs, packed, scales, x_rot
+    k, n = synth.SHAPES["gate"]
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    w = (0.02 * torch.randn((n, k), generator=gen)).to(dev)
+    signs = (torch.randint(0, 2, (k,), generator=gen) * 2 - 1).to(torch.int8).to(dev)
+    for _ in range(3):
+        tl.quantize(w, signs)
+    torch.cuda.synchronize()
+    del w, signs
+    inp = synth.linear_inputs(n, k, 1, seed=0, cfg=4, linear=synth.LINEAR_ID["gate"])
+    packed = tl.pack(torch.from_numpy(inp.codes).to(dev), 1)
+    scales = torch.from_numpy(inp.scales).to(dev)
+    x = torch.randn((4096, k), generator=gen).to(torch.bfloat16).to(dev)
+    y = torch.empty((4096, n), dtype=torch.float32, device=dev)
+    for _ in range(2):
+        tl.gemm_bf16(packed, scales, 1, x, out=y)
+    torch.cuda.synchronize()
+    log("batched profile pass done")
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -584,6 +635,9 @@ def main(argv=None) -> int:
                          "kernel, 3 launches) then 10 eager passes of the step's GEMVs; no timing")
     ap.add_argument("--read-floor", action="store_true",
                     help="time a read-only kernel at transfer sizes 4 MiB .. 512 MiB and exit")
+    ap.add_argument("--profile-batched", action="store_true",
+                    help="run only the batched-decode, quantiser and bf16 GEMM kernel set of "
+                         "the counter runs")
     ap.add_argument("--profile-prefill", action="store_true",
                     help="for counter runs under rocprofv3: the calibration copy, then the prefill "
                          "GEMM (M=4096, gate and down) and the rotation at M=4096; no timing")
@@ -610,6 +664,8 @@ def main(argv=None) -> int:
         return profile_pass(torch, tl, synth, dev, fmt)
     if args.profile_prefill:
         return profile_prefill(torch, tl, synth, dev)
+    if args.profile_batched:
+        return profile_batched(torch, tl, synth, dev)
     if args.read_floor:
         return read_floor(torch, tl, dev)
     log(f"building inputs fmt={args.fmt} copies={args.copies}")
