@@ -11,8 +11,9 @@
 //
 // One workgroup of 256 threads per (row, 1024-block); thread t holds
 // elements 4t..4t+3.  The butterflies run in fp32 in a fixed order (index
-// bits 0-1 in registers, bits 2-9 through LDS), so results are bitwise
-// reproducible.  Offline work, once per weight.
+// bits 0-1 in registers, bits 2-9 through two alternating LDS buffers, one
+// barrier per stage), so results are bitwise reproducible.  Offline work, once
+// per weight.
 #include <hip/hip_fp16.h>
 
 #include "tl_internal.h"
@@ -22,18 +23,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restrict__ w,
-                                                            const int8_t* __restrict__ signs,
-                                                            int64_t k, int8_t* __restrict__ codes,
-                                                            uint16_t* __restrict__ scales) {
-    __shared__ float buf[kBlock];
-    const int t = threadIdx.x;
-    const int64_t blocks = k / kBlock;
-    const int64_t row = blockIdx.x / blocks, blk = blockIdx.x - row * blocks;
-    const int64_t base = row * k + blk * kBlock + 4 * t;
+constexpr int kUnits = 4;   // (row, 1024-block) units per workgroup, loaded together
 
-    const float4 wv = *reinterpret_cast<const float4*>(w + base);
-    const char4 sv = *reinterpret_cast<const char4*>(signs + blk * kBlock + 4 * t);
+// One unit: elements 4t..4t+3 of row `row`, block `blk`, already loaded.
+__device__ __forceinline__ void quantize_unit(const float4 wv, const char4 sv, int64_t row,
+                                              int64_t blk, int64_t k, int t,
+                                              float (&buf)[2][kBlock], int8_t* __restrict__ codes,
+                                              uint16_t* __restrict__ scales) {
+    const int64_t base = row * k + blk * kBlock + 4 * t;
     float v[4] = {sv.x < 0 ? -wv.x : wv.x, sv.y < 0 ? -wv.y : wv.y, sv.z < 0 ? -wv.z : wv.z,
                   sv.w < 0 ? -wv.w : wv.w};
     // index bits 0 and 1: (a, b) -> (a + b, a - b)
@@ -42,18 +39,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
     v[1] = a1 + a3;
     v[2] = a0 - a2;
     v[3] = a1 - a3;
-    // index bits 2..9 (thread bits 0..7) through LDS
-    for (int bit = 2; bit < 10; ++bit) {
+    // index bits 2..9 (thread bits 0..7) through LDS, one barrier per stage
 #pragma unroll
-        for (int e = 0; e < 4; ++e) buf[4 * t + e] = v[e];
+    for (int bit = 2; bit < 10; ++bit) {
+        float* b = buf[bit & 1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) b[4 * t + e] = v[e];
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 4 * t + e;
-            const float p = buf[i ^ (1 << bit)];
+            const float p = b[i ^ (1 << bit)];
             v[e] = (i >> bit) & 1 ? p - v[e] : v[e] + p;
         }
-        __syncthreads();
     }
     float s = 0.0f;
 #pragma unroll
@@ -79,13 +77,54 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
         scales[row * (k / kGroup) + blk * (kBlock / kGroup) + (t >> 5)] = __half_as_ushort(sh);
 }
 
+// The loads of all units go out first, so a workgroup keeps kUnits x 4 KB
+// in flight; the units are then rotated and rounded one after another.
+__global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restrict__ w,
+                                                            const int8_t* __restrict__ signs,
+                                                            int64_t k, int64_t units,
+                                                            int8_t* __restrict__ codes,
+                                                            uint16_t* __restrict__ scales) {
+    // two buffers, used by alternate stages: a stage's barrier also tells every
+    // thread that the reads of the stage before the previous one are done
+    __shared__ float buf[2][kBlock];
+    const int t = threadIdx.x;
+    const int64_t blocks = k / kBlock;
+    // (row, block) of each unit: one division, then steps along the rows
+    const int64_t u0 = int64_t(blockIdx.x) * kUnits;   // workgroup-uniform
+    int64_t rows[kUnits], blks[kUnits];
+    {
+        int64_t r = u0 / blocks, b = u0 - r * blocks;
+#pragma unroll
+        for (int j = 0; j < kUnits; ++j) {
+            rows[j] = r;
+            blks[j] = b;
+            if (++b == blocks) {
+                b = 0;
+                ++r;
+            }
+        }
+    }
+    float4 wv[kUnits];
+    char4 sv[kUnits];
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j)
+        if (u0 + j < units) {
+            wv[j] = *reinterpret_cast<const float4*>(w + rows[j] * k + blks[j] * kBlock + 4 * t);
+            sv[j] = *reinterpret_cast<const char4*>(signs + blks[j] * kBlock + 4 * t);
+        }
+#pragma unroll
+    for (int j = 0; j < kUnits; ++j)
+        if (u0 + j < units) quantize_unit(wv[j], sv[j], rows[j], blks[j], k, t, buf, codes, scales);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
                            int8_t* codes, uint16_t* scales, hipStream_t stream) {
-    const int64_t blocks = n * (k / kBlock);
-    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0, stream, w,
-                       signs, k, codes, scales);
+    const int64_t units = n * (k / kBlock);
+    const int64_t grid = (units + kUnits - 1) / kUnits;
+    hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, stream, w,
+                       signs, k, units, codes, scales);
     return hipGetLastError();
 }
 
