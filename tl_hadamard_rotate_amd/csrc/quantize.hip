@@ -9,11 +9,12 @@
 //   S = binary16(mean of |w'| over a group of 128), c = rint(w' / S) clipped
 //   to [-1, 1] (ties to even: |w'| = S / 2 gives 0), c = 0 where S = 0.
 //
-// One workgroup of 256 threads per (row, 1024-block); thread t holds
-// elements 4t..4t+3.  The butterflies run in fp32 in a fixed order (index
-// bits 0-1 in registers, bits 2-9 through two alternating LDS buffers, one
-// barrier per stage), so results are bitwise reproducible.  Offline work, once
-// per weight.
+// One wave per (row, 1024-block) unit, lane l holding elements 16l .. 16l + 15:
+// index bits 0-3 are butterflied in registers and bits 4-9 (the lane bits)
+// with cross-lane permutes, so no LDS storage and no workgroup barrier are
+// needed; each wave loads its two units before working on either.
+// fp32 throughout in a fixed order, so results are bitwise reproducible.
+// Offline work, once per weight.
 #include <hip/hip_fp16.h>
 
 #include "tl_internal.h"
@@ -22,80 +23,86 @@ namespace tl {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaveUnits = 2;   // (row, 1024-block) units per wave, loaded together
 
-constexpr int kUnits = 4;   // (row, 1024-block) units per workgroup, loaded together
-
-// One unit: elements 4t..4t+3 of row `row`, block `blk`, already loaded.
-__device__ __forceinline__ void quantize_unit(const float4 wv, const char4 sv, int64_t row,
-                                              int64_t blk, int64_t k, int t,
-                                              float (&buf)[2][kBlock], int8_t* __restrict__ codes,
-                                              uint16_t* __restrict__ scales) {
-    const int64_t base = row * k + blk * kBlock + 4 * t;
-    float v[4] = {sv.x < 0 ? -wv.x : wv.x, sv.y < 0 ? -wv.y : wv.y, sv.z < 0 ? -wv.z : wv.z,
-                  sv.w < 0 ? -wv.w : wv.w};
-    // index bits 0 and 1: (a, b) -> (a + b, a - b)
-    float a0 = v[0] + v[1], a1 = v[0] - v[1], a2 = v[2] + v[3], a3 = v[2] - v[3];
-    v[0] = a0 + a2;
-    v[1] = a1 + a3;
-    v[2] = a0 - a2;
-    v[3] = a1 - a3;
-    // index bits 2..9 (thread bits 0..7) through LDS, one barrier per stage
+// One wave, one unit: lane l holds elements 16l .. 16l + 15 of the block.
+// Index bits 0-3 are butterflied in registers, bits 4-9 (lane bits 0-5)
+// across lanes; fp32 throughout in a fixed order.
+__device__ __forceinline__ void quantize_wave_unit(const float4 (&wv)[4], const uint4 sv,
+                                                   int64_t row, int64_t blk, int64_t k, int l,
+                                                   int8_t* __restrict__ codes,
+                                                   uint16_t* __restrict__ scales) {
+    float v[16];
+    const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
 #pragma unroll
-    for (int bit = 2; bit < 10; ++bit) {
-        float* b = buf[bit & 1];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[4 * t + e] = v[e];
-        __syncthreads();
+    for (int i = 0; i < 4; ++i) {
+        const float f[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 4 * t + e;
-            const float p = b[i ^ (1 << bit)];
-            v[e] = (i >> bit) & 1 ? p - v[e] : v[e] + p;
+            const int j = 4 * i + e;
+            const bool neg = (sw[j >> 2] >> (8 * (j & 3) + 7)) & 1u;
+            v[j] = neg ? -f[e] : f[e];
         }
+    }
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (!(j & h)) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        // partner values first (16 exchanges in flight), then p + sign * v:
+        // v + p in the lower lane of a pair, p - v in the upper (exact sign)
+        const float sgn = (l & m) ? -1.0f : 1.0f;
+        float p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = __shfl_xor(v[j], m, 64);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = __builtin_fmaf(v[j], sgn, p[j]);
     }
     float s = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v[e] *= 1.0f / 32.0f;
-        s += __builtin_fabsf(v[e]);
+    for (int j = 0; j < 16; ++j) {
+        v[j] *= 1.0f / 32.0f;
+        s += __builtin_fabsf(v[j]);
     }
-    // group of 128 = the 32 threads 32g .. 32g + 31 (half a wave)
-    s += __shfl_xor(s, 16, 32);
-    s += __shfl_xor(s, 8, 32);
-    s += __shfl_xor(s, 4, 32);
-    s += __shfl_xor(s, 2, 32);
-    s += __shfl_xor(s, 1, 32);
+    // group of 128 = the 8 lanes 8g .. 8g + 7
+    s += __shfl_xor(s, 4, 64);
+    s += __shfl_xor(s, 2, 64);
+    s += __shfl_xor(s, 1, 64);
     const __half sh = __float2half_rn(s * (1.0f / 128.0f));
     const float sc = __half2float(sh);
     const float half_s = 0.5f * sc;
-    int8_t c[4];
+    uint32_t cw[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        c[e] = sc != 0.0f && __builtin_fabsf(v[e]) > half_s ? (v[e] > 0.0f ? 1 : -1) : 0;
-    *reinterpret_cast<char4*>(codes + base) = char4{c[0], c[1], c[2], c[3]};
-    if ((t & 31) == 0)
-        scales[row * (k / kGroup) + blk * (kBlock / kGroup) + (t >> 5)] = __half_as_ushort(sh);
+    for (int j = 0; j < 16; ++j) {
+        const int c = sc != 0.0f && __builtin_fabsf(v[j]) > half_s ? (v[j] > 0.0f ? 1 : -1) : 0;
+        cw[j >> 2] |= (uint32_t(c) & 0xFFu) << (8 * (j & 3));
+    }
+    *reinterpret_cast<uint4*>(codes + row * k + blk * kBlock + 16 * l) = uint4{cw[0], cw[1], cw[2], cw[3]};
+    if ((l & 7) == 0)
+        scales[row * (k / kGroup) + blk * (kBlock / kGroup) + (l >> 3)] = __half_as_ushort(sh);
 }
 
-// The loads of all units go out first, so a workgroup keeps kUnits x 4 KB
-// in flight; the units are then rotated and rounded one after another.
+// Each wave handles kWaveUnits consecutive units, all of whose loads go out
+// first; no LDS and no workgroup barrier.
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restrict__ w,
                                                             const int8_t* __restrict__ signs,
                                                             int64_t k, int64_t units,
                                                             int8_t* __restrict__ codes,
                                                             uint16_t* __restrict__ scales) {
-    // two buffers, used by alternate stages: a stage's barrier also tells every
-    // thread that the reads of the stage before the previous one are done
-    __shared__ float buf[2][kBlock];
-    const int t = threadIdx.x;
+    const int l = threadIdx.x & 63;
     const int64_t blocks = k / kBlock;
-    // (row, block) of each unit: one division, then steps along the rows
-    const int64_t u0 = int64_t(blockIdx.x) * kUnits;   // workgroup-uniform
-    int64_t rows[kUnits], blks[kUnits];
+    const int64_t u0 = (int64_t(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6)) * kWaveUnits;
+    int64_t rows[kWaveUnits], blks[kWaveUnits];
     {
         int64_t r = u0 / blocks, b = u0 - r * blocks;
 #pragma unroll
-        for (int j = 0; j < kUnits; ++j) {
+        for (int j = 0; j < kWaveUnits; ++j) {
             rows[j] = r;
             blks[j] = b;
             if (++b == blocks) {
@@ -104,17 +111,19 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
             }
         }
     }
-    float4 wv[kUnits];
-    char4 sv[kUnits];
+    float4 wv[kWaveUnits][4];
+    uint4 sv[kWaveUnits];
 #pragma unroll
-    for (int j = 0; j < kUnits; ++j)
+    for (int j = 0; j < kWaveUnits; ++j)
         if (u0 + j < units) {
-            wv[j] = *reinterpret_cast<const float4*>(w + rows[j] * k + blks[j] * kBlock + 4 * t);
-            sv[j] = *reinterpret_cast<const char4*>(signs + blks[j] * kBlock + 4 * t);
+            const float4* src = reinterpret_cast<const float4*>(w + rows[j] * k + blks[j] * kBlock + 16 * l);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[j][i] = src[i];
+            sv[j] = *reinterpret_cast<const uint4*>(signs + blks[j] * kBlock + 16 * l);
         }
 #pragma unroll
-    for (int j = 0; j < kUnits; ++j)
-        if (u0 + j < units) quantize_unit(wv[j], sv[j], rows[j], blks[j], k, t, buf, codes, scales);
+    for (int j = 0; j < kWaveUnits; ++j)
+        if (u0 + j < units) quantize_wave_unit(wv[j], sv[j], rows[j], blks[j], k, l, codes, scales);
 }
 
 }  // namespace
@@ -122,7 +131,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const float* __restr
 hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
                            int8_t* codes, uint16_t* scales, hipStream_t stream) {
     const int64_t units = n * (k / kBlock);
-    const int64_t grid = (units + kUnits - 1) / kUnits;
+    const int64_t per_wg = int64_t(kThreads / 64) * kWaveUnits;
+    const int64_t grid = (units + per_wg - 1) / per_wg;
     hipLaunchKernelGGL(quantize_kernel, dim3(unsigned(grid)), dim3(kThreads), 0, stream, w,
                        signs, k, units, codes, scales);
     return hipGetLastError();
