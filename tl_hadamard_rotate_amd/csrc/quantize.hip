@@ -11,8 +11,12 @@
 //
 // One wave per (row, 1024-block) unit, lane l holding elements 16l .. 16l + 15:
 // index bits 0-3 are butterflied in registers and bits 4-9 (the lane bits)
-// with cross-lane permutes, so no LDS storage and no workgroup barrier are
-// needed; each wave loads its two units before working on either.
+// with cross-lane exchanges, so no LDS storage and no workgroup barrier are
+// needed; each wave loads its two units before working on either.  The
+// exchanges are split between the VALU (DPP quad permutes for lane bits 0-1, a
+// swap of the wave's halves for bit 5) and the LDS unit's lane permute (bits
+// 2-4): all of them through the permute was bound by it, all of them on the
+// VALU by the VALU.
 // fp32 throughout in a fixed order, so results are bitwise reproducible.
 // Offline work, once per weight.
 #include <hip/hip_fp16.h>
@@ -24,6 +28,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaveUnits = 2;   // (row, 1024-block) units per wave, loaded together
+
+// v of lane l ^ m: DPP quad permutes for m = 1, 2, a swap of the wave's
+// halves for m = 32, a lane permute otherwise
+__device__ __forceinline__ float lane_xor(float v, int m, int l) {
+    const int b = __builtin_bit_cast(int, v);
+    if (m == 1) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, false));
+    if (m == 2) return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, false));
+    if (m == 32) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(uint32_t(b), uint32_t(b), false, false);
+        return __builtin_bit_cast(float, l < 32 ? sw[1] : sw[0]);
+    }
+    return __shfl_xor(v, m, 64);
+}
 
 // One wave, one unit: lane l holds elements 16l .. 16l + 15 of the block.
 // Index bits 0-3 are butterflied in registers, bits 4-9 (lane bits 0-5)
@@ -60,7 +77,7 @@ __device__ __forceinline__ void quantize_wave_unit(const float4 (&wv)[4], const 
         const float sgn = (l & m) ? -1.0f : 1.0f;
         float p[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) p[j] = __shfl_xor(v[j], m, 64);
+        for (int j = 0; j < 16; ++j) p[j] = lane_xor(v[j], m, l);
 #pragma unroll
         for (int j = 0; j < 16; ++j) v[j] = __builtin_fmaf(v[j], sgn, p[j]);
     }
