@@ -105,12 +105,18 @@ __device__ __forceinline__ void vm_lds_barrier() {
 }
 
 __device__ __forceinline__ void build_lut(uint8_t* lut, int tid, int nthreads) {
-    // table rows: consecutive threads write consecutive 16-byte pieces
-    for (int c = tid; c < kLutBytes / 16; c += nthreads) {
-        const uint32_t b = uint32_t(c) >> 4;
+    // Thread t fills row b = t / 4 (16 pieces of 16 bytes, two copies each):
+    // it decodes byte b once and writes pieces r, r + 4, r + 8 and r + 12
+    // (r = t % 4), starting with piece (r + 4 b) % 16, so the 16 lanes that an
+    // LDS write serves together hit 16 distinct 16-byte bank groups.
+    for (int t = tid; t < 4 * kLutRows; t += nthreads) {
+        const uint32_t b = uint32_t(t) >> 2, r = uint32_t(t) & 3u;
         const uint32_t lo = code_bits(b & 3u) | (code_bits((b >> 2) & 3u) << 16);
         const uint32_t hi = code_bits((b >> 4) & 3u) | (code_bits((b >> 6) & 3u) << 16);
-        reinterpret_cast<uint4*>(lut)[c] = uint4{lo, hi, lo, hi};
+        const uint4 e = uint4{lo, hi, lo, hi};
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i)
+            reinterpret_cast<uint4*>(lut)[b * 16 + ((r + 4 * (b + i)) & 15u)] = e;
     }
 }
 
