@@ -4,8 +4,8 @@ A step is one decode pass (M = 1) over the 27B-class MLP projections
 gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120): for
 each projection the signed 1024-block Hadamard rotation of its input and the
 ternary product (tl_linear: one fused kernel per projection with either
-packing).  Inputs are
-seeded synthetic tensors with the workload's distributions.
+packing).  Inputs are seeded synthetic tensors with the workload's
+distributions.
 
 Timing.  Each step is captured once in a HIP graph; the weights are replicated
 into --copies distinct buffers (one graph per copy) and the timed loop cycles
@@ -15,13 +15,13 @@ launch stream, with a device synchronisation on both sides.
 
 Dominant kernel (roofline): the fused tl_linear kernel, whose three launches
 make up the step; average launch time between HIP events on the launch
-stream.  HBM traffic comes from the rocprofv3
-counter summary under profiles/ and is reported only while the kernel source
-is the one those counters were taken from.
+stream.  HBM traffic comes from the rocprofv3 counter summary under
+profiles/ and is reported only while the kernel source is the one those
+counters were taken from.
 
 Extras: the other packing, the prefill GEMM sweep (and its bfloat16 variant
-at M = 4096), batched decode over the
-attention projections, the rotation at prefill size, the 64-layer weight
+at M = 4096), batched decode over the attention projections, the rotation
+at prefill size, the 64-layer weight
 stream (one rotation per linear, and one per input with q|k|v and gate|up
 concatenated), the weight quantiser, the decode step with 1-bit weights, and
 the CPU oracle on a bounded sample.
