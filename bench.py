@@ -235,14 +235,17 @@ def bench_gemm(torch, tl, synth, dev, fmt, reps=5, bf16=False, ms_list=None):
             gen = torch.Generator(device="cpu").manual_seed(4 + m)
             x = torch.randn((m, k), generator=gen).to(xdt).to(dev)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
-            call(packed, scales, fmt, x, out=y)
+            ws = torch.empty(max(1, tl.gemm_workspace_bytes(m, n, k, fmt)), dtype=torch.uint8,
+                             device=dev)
+            call(packed, scales, fmt, x, out=y, workspace=ws)
             torch.cuda.synchronize()
-            ms = _event_time(torch, lambda i: call(packed, scales, fmt, x, out=y), reps)
+            ms = _event_time(torch, lambda i: call(packed, scales, fmt, x, out=y, workspace=ws),
+                             reps)
             tflops = 2.0 * m * n * k / (ms * 1e-3) / 1e12
             out.append({"linear": name, "M": m, "K": k, "N": n, "ms": round(ms, 4),
                         "TFLOPs": round(tflops, 2),
                         "frac_of_fp16_peak": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)})
-            del x, y
+            del x, y, ws
         del packed, scales
     torch.cuda.empty_cache()
     return out
@@ -482,12 +485,26 @@ def bench_quantize(torch, tl, synth, dev, reps=10):
     return out
 
 
+def probe_lib():
+    """The benchmark's read-only probe (libtl_probe.so, built beside libtl)."""
+    import ctypes
+    path = os.path.join(ROOT, "tl_hadamard_rotate_amd", "libtl_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m tl_hadamard_rotate_amd.build`")
+    L = ctypes.CDLL(path)
+    L.tlprobe_stream_read.restype = ctypes.c_int
+    L.tlprobe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_int32, ctypes.c_void_p]
+    return L
+
+
 def read_floor(torch, tl, dev, reps=20) -> int:
-    """What HBM delivers to a read-only kernel (tl_stream_read) at transfer
+    """What HBM delivers to a read-only kernel (tlprobe_stream_read) at transfer
     sizes from 4 MiB to 512 MiB, including the 23.8 MB one gate/up decode
     launch reads: buffers cycled through a 1 GiB pool, average time per
     launch between HIP events (the rocprofv3 trace of this mode gives the
     kernel durations).  Prints one JSON line."""
+    probe = probe_lib()
     pool_bytes = 1 << 30
     pool = torch.empty(pool_bytes, dtype=torch.uint8, device=dev).fill_(1)
     out = torch.full((65,), 0x5A5A5A5A, dtype=torch.int32, device=dev)   # out[0]: the key
@@ -500,9 +517,9 @@ def read_floor(torch, tl, dev, reps=20) -> int:
 
         def call(i):
             ptr = pool.data_ptr() + (i % slots) * b
-            st = tl.lib().tl_stream_read(ptr, b, out.data_ptr(), blocks, stream)
+            st = probe.tlprobe_stream_read(ptr, b, out.data_ptr(), blocks, stream)
             if st != 0:
-                raise RuntimeError(f"tl_stream_read failed: {st}")
+                raise RuntimeError(f"tlprobe_stream_read failed: {st}")
         call(0)
         torch.cuda.synchronize()
         ms = _event_time(torch, call, reps)

@@ -17,7 +17,8 @@
  *
  * Conventions shared by every call
  *   - All tensors are dense row-major device buffers owned by the caller; the
- *     library never allocates, frees or retains them.
+ *     library never allocates, frees or retains device memory.  The prefill
+ *     products take a caller-owned workspace (tl_gemm_workspace_bytes).
  *   - binary16 data is passed as uint16_t (bit patterns).
  *   - Every call validates its arguments first.  On a validation failure it
  *     returns the status and launches nothing, so outputs are untouched.
@@ -25,8 +26,8 @@
  *     call returns TL_OK without synchronising.  A launch failure returns
  *     TL_ERR_LAUNCH and tl_last_error() gives the HIP error text (per thread).
  *   - The library keeps no state between calls apart from that per-thread
- *     error text and the K-split workspace of tl_gemm (below); calls from
- *     several threads are safe.
+ *     error text and, per device, the compute-unit count and the kernels' LDS
+ *     limits, looked up on first use; calls from several threads are safe.
  *
  * Formats (bit-exact; defined here, since the pages give no byte layout)
  *   digit d = code + 1, in {0, 1, 2}.
@@ -41,6 +42,11 @@
  *     row holds K/8 bytes and bit i of byte j holds b[8j+i].  1.125 bits per
  *     weight with the scales (page "How Prism ML Squeezed a 27B Model Into
  *     3.9 GB", list "Two formats ship today").
+ *   Packed bytes that are not valid encodings (a 2-bit slot holding 3, a
+ *     dense-trit byte above 242, a group's last byte whose pad digits are not
+ *     1) give unspecified results in every call that reads packed codes (the
+ *     kernels stay within their buffers).  tl_pack never writes such bytes; it
+ *     counts the invalid codes it was given in bad_count.
  *   Scales: binary16 [N, K/128]; weight (n, k) = code * scales[n, k/128].
  *   Signs: int8 [K] of +1/-1; block b of the rotation uses signs[1024b .. +1023].
  */
@@ -68,7 +74,8 @@ typedef enum {
     TL_ERR_ALIGN = 4,    /* a pointer is not 16-byte aligned                   */
     TL_ERR_ALIAS = 5,    /* an output overlaps an input it must not overlap    */
     TL_ERR_LAUNCH = 6,   /* the HIP launch failed; see tl_last_error()         */
-    TL_ERR_DTYPE = 7     /* unknown output dtype                               */
+    TL_ERR_DTYPE = 7,    /* unknown output dtype                               */
+    TL_ERR_WORKSPACE = 8 /* workspace missing or smaller than the call needs   */
 } tl_status;
 
 enum { TL_FMT_TRIT5 = 0, TL_FMT_SLOT2 = 1, TL_FMT_BIT1 = 2 };
@@ -125,25 +132,42 @@ TL_API tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t 
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
                   void* y, int32_t y_dtype, hipStream_t stream);
 
+/* Bytes of device workspace that tl_gemm, tl_gemm_bf16 and tl_linear need
+ * for this shape and format (0: none; tl_gemm_bf16 and tl_linear at M < 64
+ * need at most this much).  Host only; it depends on the compute-unit count of
+ * the current device.  Returns -1 when the shape or format is not accepted
+ * (tl_gemm's rules).  The workspace holds, for dense trits and 1-bit codes,
+ * the weights rewritten as 2-bit slots (N * K/4 bytes, rounded up to 256),
+ * then, when output tiles are split along K, their fp32 partial sums (at most
+ * 64 MiB). */
+TL_API int64_t tl_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
+
+/* Launch plan of tl_gemm for this shape (host only, for tests and tuning):
+ * out[0] = output tiles of 256 x 256, out[1] = tiles computed whole, out[2] =
+ * parts along K of each remaining tile.  Returns TL_OK, TL_ERR_NULL or
+ * TL_ERR_SHAPE (tl_gemm's shape rules). */
+TL_API tl_status tl_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t* out);
+
 /* Same operation and argument rules as tl_gemv, tuned for prefill (M >= 64):
  * weight tiles are expanded to exact binary16 (code * scale) on chip and fed
  * to fp16 matrix-core instructions with fp32 accumulation.  Prompt processing
  * is where the pages place the practical bottleneck on slower chips (Persian
  * page, paragraph 4).
- * With TL_FMT_SLOT2, output tiles that would leave most of the GPU idle in a
- * last partial round are split along K; their fp32 partial sums go to a
- * workspace the library owns, one per (device, stream), and a second kernel
- * adds them in a fixed order (results do not depend on scheduling).  The
- * workspace is allocated with hipMalloc the first time a call needs it or
- * more of it (so such a call cannot be captured into a HIP graph; later
- * calls of equal or smaller shape allocate nothing) and is never freed before
- * the process ends (under 1 GiB: at most 16 parts of 256 KB for each of
- * fewer tiles than the GPU has compute units).  With TL_FMT_TRIT5 the
- * weights are first rewritten as 2-bit slots (same codes; N * K/4 bytes) into
- * a second such workspace, then multiplied the same way. */
+ * Output tiles that would leave most of the GPU idle in a last partial round
+ * are split along K; their fp32 partial sums go to the workspace and a second
+ * kernel adds them in a fixed order (results do not depend on scheduling).
+ * Dense trits and 1-bit codes are first rewritten as 2-bit slots (same codes)
+ * into the workspace, then multiplied the same way.
+ * workspace: caller-owned device memory of workspace_bytes >=
+ * tl_gemm_workspace_bytes(M, N, K, fmt) bytes (may be NULL when that is 0),
+ * 16-byte aligned, overlapping no argument; its contents on entry do not
+ * matter, and calls that may run at the same time need separate workspaces.
+ * Too small: TL_ERR_WORKSPACE.  Additionally requires M * K < 2^31 and
+ * N * K / 4 < 2^32 (TL_ERR_SHAPE). */
 TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
-                  void* y, int32_t y_dtype, hipStream_t stream);
+                  void* y, int32_t y_dtype, void* workspace, int64_t workspace_bytes,
+                  hipStream_t stream);
 
 /* The whole layer on unrotated activations:
  *   x_rot = R(x)  (as tl_hadamard_rotate),   y = dequant(codes, scales) . x_rot
@@ -159,27 +183,29 @@ TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t 
  * most N) the rotation runs inside the GEMV kernel: one launch, the rotated
  * activations never make a round trip through memory before use (x_rot is
  * still written).  Otherwise: tl_hadamard_rotate, then tl_gemv (M < 64) or
- * tl_gemm (M >= 64).
+ * tl_gemm (M >= 64, with the workspace as tl_gemm; unused below 64).
  * Linears that read the same input (q, k, v; gate, up) share its rotation:
  * the signs belong to the input, so their packed rows and scales can be
  * concatenated along N (row-major, so plain concatenation) and run as one
  * call, which rotates once and launches once. */
 TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                     const uint16_t* x, const int8_t* signs, int64_t M, int64_t N, int64_t K,
-                    uint16_t* x_rot, void* y, int32_t y_dtype, hipStream_t stream);
+                    uint16_t* x_rot, void* y, int32_t y_dtype, void* workspace,
+                    int64_t workspace_bytes, hipStream_t stream);
 
 /* The prefill product with bfloat16 rotated activations:
  *   y[m, n] = sum_g S[n, g] * sum_{k in g} code[n, k] * x_rot[m, k]
  * with the codes entering the matrix cores as exact bfloat16 -1/0/+1 and each
  * group's fp32 sum multiplied by its binary16 scale in fp32 (the scale is not
  * rounded to bfloat16).  x_rot: bfloat16 [M, K] passed as uint16 bits; every
- * other argument, rule and error as tl_gemm (the same workspace for dense
- * trits and 1-bit codes, which are rewritten as 2-bit slots first).  For
+ * other argument, rule and error as tl_gemm (the workspace holds only the
+ * rewrite of dense trits and 1-bit codes as 2-bit slots; no K split).  For
  * models whose activations are bfloat16; the binary16 tl_gemm is the more
  * accurate product (bfloat16 keeps 8 significant bits against 11). */
 TL_API tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                               const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
-                              int32_t y_dtype, hipStream_t stream);
+                              int32_t y_dtype, void* workspace, int64_t workspace_bytes,
+                              hipStream_t stream);
 
 /* Quantise real-valued weight rows to ternary g128, the rotation folded in
  * (page "OpenBonsai", section "How it works", steps 1 and 2: rotate with the
@@ -199,15 +225,6 @@ TL_API tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int
                              int8_t* codes, uint16_t* scales, hipStream_t stream);
 
 /* Static name of a status code ("TL_OK", ...). */
-/* Measurement helper, not part of the layer: read `bytes` of device memory
- * (16-byte aligned, a multiple of 16) with `blocks` workgroups of 256 threads
- * (1..65536).  out: uint32 [65] (device, not overlapping buf); out[0] is a
- * key, and a lane whose xor of its words equals it writes out[1..64].
- * Timing it gives what HBM delivers to a read-only kernel at that transfer
- * size, the floor for the memory-bound kernels. */
-TL_API tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
-                                hipStream_t stream);
-
 TL_API const char* tl_status_str(tl_status status);
 
 /* Text of the last TL_ERR_LAUNCH on the calling thread ("" if none). */

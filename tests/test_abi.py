@@ -23,7 +23,8 @@ def _declared():
 
 def test_header_declares_the_four_calls():
     names = _declared()
-    for need in ("tl_pack", "tl_hadamard_rotate", "tl_gemv", "tl_gemm", "tl_linear", "tl_quantize"):
+    for need in ("tl_pack", "tl_hadamard_rotate", "tl_gemv", "tl_gemm", "tl_linear", "tl_quantize",
+                 "tl_gemm_workspace_bytes", "tl_gemm_plan"):
         assert need in names
 
 
@@ -53,9 +54,14 @@ def test_status_strings():
         assert L.tl_status_str(code).decode() == name
 
 
+WS = A + 0x10000000        # a fake workspace far from every other buffer
+
+
 def _gemv(fn, packed=A, scales=A + 0x1000000, fmt=0, x=A + 0x2000000, m=1, n=64, k=1024,
-          y=A + 0x3000000, yd=0):
-    return fn(packed, scales, fmt, x, m, n, k, y, yd, NULL)
+          y=A + 0x3000000, yd=0, ws=WS, ws_bytes=1 << 30):
+    if fn.__name__ == "tl_gemv":
+        return fn(packed, scales, fmt, x, m, n, k, y, yd, NULL)
+    return fn(packed, scales, fmt, x, m, n, k, y, yd, ws, ws_bytes, NULL)
 
 
 @pytest.mark.parametrize("call", ["tl_gemv", "tl_gemm"])
@@ -84,8 +90,9 @@ def test_linear_validation():
     f = tl.lib().tl_linear
     P, S, X, G, XR, Y = A, A + 0x1000000, A + 0x2000000, A + 0x2800000, A + 0x3000000, A + 0x4000000
 
-    def call(packed=P, scales=S, fmt=1, x=X, signs=G, m=1, n=1024, k=1024, x_rot=XR, y=Y, yd=0):
-        return f(packed, scales, fmt, x, signs, m, n, k, x_rot, y, yd, NULL)
+    def call(packed=P, scales=S, fmt=1, x=X, signs=G, m=1, n=1024, k=1024, x_rot=XR, y=Y, yd=0,
+             ws=NULL, ws_bytes=0):
+        return f(packed, scales, fmt, x, signs, m, n, k, x_rot, y, yd, ws, ws_bytes, NULL)
 
     assert call(signs=NULL) == 1
     assert call(x_rot=NULL) == 1
@@ -99,6 +106,51 @@ def test_linear_validation():
     assert call(x_rot=Y - 16) == 5       # into y
     assert call(y=G) == 5                # y over the signs
     assert call(yd=2) == 7
+    # prefill (M >= 64) with dense trits needs the workspace of tl_gemm
+    need = tl.lib().tl_gemm_workspace_bytes(64, 1024, 1024, 0)
+    assert need >= 1024 * 1024 // 4
+    assert call(fmt=0, m=64, n=1024) == 8
+    assert call(fmt=0, m=64, n=1024, ws=WS, ws_bytes=need - 1) == 8
+    assert call(fmt=0, m=64, n=1024, ws=WS + 8, ws_bytes=need) == 4
+    assert call(fmt=0, m=64, n=1024, ws=XR, ws_bytes=need) == 5
+
+
+def test_gemm_workspace_and_plan():
+    L = tl.lib()
+    # dense trits and 1-bit codes: the 2-bit-slot rewrite of the weights comes
+    # first; the fp32 partial sums of K-split tiles (256 x 256 floats each)
+    # after it, on a 256-byte boundary
+    for m, n, k in [(64, 1024, 1024), (512, 17408, 5120), (512, 5120, 17408), (4096, 5120, 17408)]:
+        out = (ctypes.c_int64 * 3)()
+        assert L.tl_gemm_plan(m, n, k, out) == 0
+        tiles, whole, splits = out[0], out[1], out[2]
+        assert tiles == -(-m // 256) * -(-n // 256)
+        assert 0 <= whole <= tiles and 1 <= splits <= 16
+        assert (splits == 1) == (whole == tiles)
+        partial = (tiles - whole) * splits * 256 * 256 * 4 if splits > 1 else 0
+        assert partial <= 64 << 20
+        assert L.tl_gemm_workspace_bytes(m, n, k, 1) == partial
+        rewrite = -(-(n * k // 4) // 256) * 256
+        assert L.tl_gemm_workspace_bytes(m, n, k, 0) == rewrite + partial
+        assert L.tl_gemm_workspace_bytes(m, n, k, 2) == rewrite + partial
+    assert L.tl_gemm_workspace_bytes(64, 1024, 1000, 1) == -1
+    assert L.tl_gemm_workspace_bytes(64, 1024, 1024, 9) == -1
+    assert L.tl_gemm_plan(64, 1024, 1024, NULL) == 1
+    out = (ctypes.c_int64 * 3)()
+    assert L.tl_gemm_plan(0, 1024, 1024, out) == 2
+    assert L.tl_gemm_plan(1 << 20, 1024, 4096, out) == 2      # M * K reaches 2^31
+
+
+@pytest.mark.parametrize("call", ["tl_gemm", "tl_gemm_bf16"])
+def test_gemm_workspace_validation(call):
+    fn = getattr(tl.lib(), call)
+    need = tl.lib().tl_gemm_workspace_bytes(64, 1024, 1024, 0)
+    rewrite = 1024 * 1024 // 4        # all tl_gemm_bf16 needs: no K split
+    assert _gemv(fn, m=64, n=1024, ws=NULL, ws_bytes=0) == 8            # missing
+    assert _gemv(fn, m=64, n=1024, ws_bytes=rewrite - 1) == 8            # too small
+    assert _gemv(fn, m=64, n=1024, ws=WS + 4, ws_bytes=need) == 4        # misaligned
+    assert _gemv(fn, m=64, n=1024, ws=A + 0x2000000, ws_bytes=need) == 5  # over x
+    assert _gemv(fn, m=64, n=1024, ws=A + 0x3000000 - 16, ws_bytes=need) == 5   # into y
 
 
 def test_rotate_validation():
@@ -163,10 +215,18 @@ def test_gemm_bf16_validation():
     assert _gemv(fn, yd=3) == 7
 
 
-def test_stream_read_validation():
-    f = tl.lib().tl_stream_read
+def test_layer_library_exports_no_probe():
+    """The benchmark's read-only probe lives in its own library."""
+    lib = ctypes.CDLL(tl.LIB_PATH)
+    assert not hasattr(lib, "tl_stream_read")
+
+
+def test_probe_library_validation():
+    f = ctypes.CDLL(os.path.join(os.path.dirname(tl.LIB_PATH), "libtl_probe.so")).tlprobe_stream_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
     assert f(NULL, 1024, A, 4, NULL) == 1
-    assert f(A, 1000, A + 0x100000, 4, NULL) == 2
-    assert f(A, 1024, A + 0x100000, 0, NULL) == 2
-    assert f(A + 8, 1024, A + 0x100000, 4, NULL) == 4
-    assert f(A, 1024, A + 16, 4, NULL) == 5
+    assert f(A, 1000, A + 0x100000, 4, NULL) == 1
+    assert f(A, 1024, A + 0x100000, 0, NULL) == 1
+    assert f(A + 8, 1024, A + 0x100000, 4, NULL) == 1
+    assert f(A, 1024, A + 16, 4, NULL) == 1

@@ -26,7 +26,8 @@ BLOCK = 1024
 GROUP = 128
 
 _STATUS = {0: "TL_OK", 1: "TL_ERR_NULL", 2: "TL_ERR_SHAPE", 3: "TL_ERR_FORMAT",
-           4: "TL_ERR_ALIGN", 5: "TL_ERR_ALIAS", 6: "TL_ERR_LAUNCH", 7: "TL_ERR_DTYPE"}
+           4: "TL_ERR_ALIGN", 5: "TL_ERR_ALIAS", 6: "TL_ERR_LAUNCH", 7: "TL_ERR_DTYPE",
+           8: "TL_ERR_WORKSPACE"}
 
 _lib = None
 
@@ -56,11 +57,12 @@ def lib() -> ctypes.CDLL:
             "tl_unpack": (i32, [p, i64, i64, i32, p, p]),
             "tl_hadamard_rotate": (i32, [p, p, i64, i64, p, p]),
             "tl_gemv": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
-            "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
-            "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p]),
+            "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p, i64, p]),
+            "tl_gemm_workspace_bytes": (i64, [i64, i64, i64, i32]),
+            "tl_gemm_plan": (i32, [i64, i64, i64, p]),
+            "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p, i64, p]),
             "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
-            "tl_gemm_bf16": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
-            "tl_stream_read": (i32, [p, i64, p, i32, p]),
+            "tl_gemm_bf16": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p, i64, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }
@@ -162,7 +164,38 @@ def quantize(w: torch.Tensor, signs: torch.Tensor):
     return codes, scales
 
 
-def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch.float16):
+def gemm_workspace_bytes(m: int, n: int, k: int, fmt: int) -> int:
+    """Device workspace bytes tl_gemm / tl_gemm_bf16 / tl_linear need (0: none)."""
+    b = int(lib().tl_gemm_workspace_bytes(m, n, k, fmt))
+    if b < 0:
+        raise TLError("tl_gemm_workspace_bytes", 2)
+    return b
+
+
+def gemm_plan(m: int, n: int, k: int) -> tuple[int, int, int]:
+    """tl_gemm's launch plan: (output tiles, tiles computed whole, K parts of
+    each remaining tile)."""
+    out = (ctypes.c_int64 * 3)()
+    _check("tl_gemm_plan", lib().tl_gemm_plan(m, n, k, out))
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def _workspace(m, n, k, fmt, device, workspace):
+    """(pointer, bytes) of the workspace a prefill call needs: the caller's
+    uint8 tensor when given, else one from torch's allocator (None when the
+    call needs none)."""
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, 1)
+        return _ptr(workspace), workspace.numel(), workspace
+    need = gemm_workspace_bytes(m, n, k, fmt)
+    if need == 0:
+        return _ptr(None), 0, None
+    ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return _ptr(ws), need, ws
+
+
+def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch.float16,
+            workspace=None):
     _need(packed, "packed", torch.uint8, 2)
     _need(scales, "scales", torch.float16, 2)
     _need(x_rot, "x_rot", x_dtype, 2)
@@ -182,8 +215,13 @@ def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch
             raise ValueError("out must be [M, N]")
     yd = TL_F32 if out_dtype == torch.float32 else TL_F16
     fn = getattr(lib(), call)
-    _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
-                    _stream(x_rot)))
+    if call == "tl_gemv":
+        _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
+                        _stream(x_rot)))
+    else:
+        wp, wb, _keep = _workspace(m, n, k, fmt, x_rot.device, workspace)
+        _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
+                        wp, wb, _stream(x_rot)))
     return out
 
 
@@ -192,20 +230,24 @@ def gemv(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch
     return _linear("tl_gemv", packed, scales, fmt, x_rot, out_dtype, out)
 
 
-def gemm_bf16(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
+def gemm_bf16(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None,
+              workspace=None) -> torch.Tensor:
     """The prefill product with bfloat16 rotated activations x_rot [M, K]:
     codes as bfloat16 -1/0/+1 on the matrix cores, group scales in fp32."""
     return _linear("tl_gemm_bf16", packed, scales, fmt, x_rot, out_dtype, out,
-                   x_dtype=torch.bfloat16)
+                   x_dtype=torch.bfloat16, workspace=workspace)
 
 
-def gemm(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
-    """Same as ``gemv``, prefill-shaped (large M)."""
-    return _linear("tl_gemm", packed, scales, fmt, x_rot, out_dtype, out)
+def gemm(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None,
+         workspace=None) -> torch.Tensor:
+    """Same as ``gemv``, prefill-shaped (large M).  ``workspace`` (uint8, at
+    least ``gemm_workspace_bytes``) is taken from torch's allocator when not
+    given."""
+    return _linear("tl_gemm", packed, scales, fmt, x_rot, out_dtype, out, workspace=workspace)
 
 
 def linear(packed, scales, fmt, x, signs, out_dtype=torch.float32, out=None,
-           x_rot=None) -> torch.Tensor:
+           x_rot=None, workspace=None) -> torch.Tensor:
     """y[M, N] = R(x) . dequant(codes, scales)^T on unrotated fp16 x [M, K];
     x_rot (allocated when None) receives R(x).  One fused launch at M = 1
     with the 2-bit-slot and dense trit packings (within their K limits)."""
@@ -236,8 +278,12 @@ def linear(packed, scales, fmt, x, signs, out_dtype=torch.float32, out=None,
         if out.shape != (m, n):
             raise ValueError("out must be [M, N]")
     yd = TL_F32 if out_dtype == torch.float32 else TL_F16
+    if m >= 64:
+        wp, wb, _keep = _workspace(m, n, k, fmt, x.device, workspace)
+    else:
+        wp, wb = _ptr(None), 0
     _check("tl_linear", lib().tl_linear(_ptr(packed), _ptr(scales), fmt, _ptr(x), _ptr(signs), m,
-                                        n, k, _ptr(x_rot), _ptr(out), yd, _stream(x)))
+                                        n, k, _ptr(x_rot), _ptr(out), yd, wp, wb, _stream(x)))
     return out
 
 

@@ -3,7 +3,10 @@
     python -m tl_hadamard_rotate_amd.build          # compile every csrc/*.hip
 
 Objects go to tl_hadamard_rotate_amd/_build/, the library to
-tl_hadamard_rotate_amd/libtl.so (both git-ignored).  Always recompiles.
+tl_hadamard_rotate_amd/libtl.so (both git-ignored).  The benchmark's
+read-only probe (probe/*.hip) becomes a library of its own,
+libtl_probe.so, so that it is not part of the layer library.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -16,8 +19,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
+PROBE = os.path.join(PKG, "probe")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtl.so")
+PROBE_LIB = os.path.join(PKG, "libtl_probe.so")
 ARCH = "gfx950"
 
 # packed fp32 VALU instructions are kept out of the generated code
@@ -35,12 +40,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtl)")
 
 
-def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC) -> list[str]:
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+    sub = os.path.basename(os.path.dirname(src))
+    obj = os.path.join(BUILD, sub + "_" + os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -48,19 +54,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, probes = sources(CSRC), sources(PROBE)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probes))) as ex:
+        objs = list(ex.map(_compile, srcs + probes))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources and {PROBE_LIB} from {len(probes)}")
     return LIB
 
 

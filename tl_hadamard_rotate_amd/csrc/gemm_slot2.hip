@@ -1,12 +1,13 @@
 // Prefill ternary g128 GEMM for the 2-bit-slot packing:
 //   y[m, n] = sum_k x[m, k] * code[n, k] * S[n, k/128].
-// The weights never pass through LDS: every wave loads the packed bytes of its
-// own 64 weight rows and decodes them in registers, straight into the B
-// operand of v_mfma_f32_32x32x16_f16, as exact binary16 values code * S (a code
-// in {-1, 0, 1} times a binary16 scale is a binary16 number).  Only the
-// activations, which every wave of a column of the tile shares, are staged in
-// LDS.  Prompt processing is the bottleneck the pages name for slower chips
-// (page "A 27-billion model that fits in 8.6 GB", paragraph 4).
+// The weights reach the matrix cores without an fp16 copy in LDS: their packed
+// bytes are staged in LDS (0.25 byte per weight), and every wave reads the
+// bytes of its own 64 weight rows and decodes them in registers, straight into
+// the B operand of v_mfma_f32_32x32x16_f16, as exact binary16 values code * S
+// (a code in {-1, 0, 1} times a binary16 scale is a binary16 number).  The
+// activations, which every wave of a row of the tile shares, are staged in LDS
+// as they are.  Prompt processing is the bottleneck the pages name for slower
+// chips (page "A 27-billion model that fits in 8.6 GB", paragraph 4).
 //
 // Tiling: a workgroup of 8 waves (two per SIMD) computes a 256 x 256 output
 // tile (M x N); wave w owns the 128 x 64 sub-tile (w / 4, w % 4): 4 x 2 MFMA
@@ -34,11 +35,12 @@
 // yields the binary16 pair (code0 * S, code1 * S) exactly (digit 3, which the
 // packer never writes, decodes to 0).  About 1.6 VALU operations per weight.
 //
-// Activation and weight loads run two steps ahead in a ring of registers;
-// the scales one block (4 steps) ahead.  Activations pass through two
-// LDS stages with one barrier per step.  Workgroups are mapped so that each
-// XCD (blockIdx % 8) runs a contiguous run of tiles, N fastest: concurrent
-// workgroups of an XCD share activation rows in that XCD's L2.
+// Activations, packed weights and scales go from memory straight into LDS
+// (global_load_lds) through four stages, three steps ahead of their use, with
+// one barrier per step; the scales of a block of 4 steps one block ahead.
+// Workgroups are mapped so that each XCD (blockIdx % 8) runs a contiguous run
+// of tiles, N fastest: concurrent workgroups of an XCD share activation rows
+// in that XCD's L2.
 #include <hip/hip_fp16.h>
 
 #include <type_traits>
@@ -467,9 +469,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 
 // Sum of the K parts of the split tiles, in part order (so the result does
 // not depend on the order the parts ran in), stored to y.  Block b handles
-// register e = b % 256 of split tile t0 + b / 256 for all 256 threads of the
-// GEMM's workgroup layout: thread tid holds that register of wave tid / 64 at
-// the same place as there.
+// accumulator register e = b % kRegs of split tile t0 + b / kRegs for all
+// kThreads threads of the GEMM's workgroup layout: thread tid holds that
+// register of wave tid / 64 at the same place as there.
 __global__ __launch_bounds__(kThreads) void gemm_slot2_reduce(const float* __restrict__ ws,
                                                               int64_t m, int64_t n, void* __restrict__ y,
                                                               int y_f16, int tiles_n, int t0, int splits) {
@@ -506,74 +508,60 @@ namespace {
 // K split of the tiles that do not fill a whole round of workgroups (one per
 // CU).  Cost model in units of the loop (8 steps, about 14 us of one
 // workgroup): rounds of parts of ceil(units / splits) units, plus the partial
-// sums written and read back (512 KB per part, about 0.01 unit at the HBM
-// rate) and the reducing launch (0.3 unit).
-struct Plan {
-    int t0, splits;
-};
+// sums written and read back (256 KB per part, about 0.01 unit at the HBM
+// rate) and the reducing launch (0.3 unit).  At most kMaxSplitItems parts in
+// all, so the partial sums never need more than 64 MiB of workspace.
+constexpr int64_t kMaxSplitItems = 256;
 
-Plan plan_split(int64_t tiles, int units, int cus) {
+Gemm2Plan plan_split(int64_t tiles, int units, int cus) {
     const int64_t rem = tiles % cus;
-    Plan best{int(tiles), 1};
+    Gemm2Plan best{tiles, tiles, 1};
     if (rem == 0) return best;
     double best_cost = units;
-    for (int s = 2; s <= 16 && s <= units; ++s) {
+    for (int s = 2; s <= 16 && s <= units && rem * s <= kMaxSplitItems; ++s) {
         const int64_t rounds = (rem * s + cus - 1) / cus;
         const double cost = double(rounds) * double((units + s - 1) / s) + 0.01 * double(rem * s) + 0.3;
         if (cost < best_cost - 0.5) {
             best_cost = cost;
-            best = Plan{int(tiles - rem), s};
+            best = Gemm2Plan{tiles, tiles - rem, s};
         }
     }
     return best;
 }
 
-int cu_count() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-            cus = n;
-        else
-            return 256;
-    }
-    return cus;
-}
-
 }  // namespace
 
+Gemm2Plan gemm_slot2_plan(int64_t m, int64_t n, int64_t k) {
+    const int64_t tiles = ((m + BM - 1) / BM) * ((n + BN - 1) / BN);
+    return plan_split(tiles, int(k / 512), cu_count());
+}
+
+int64_t gemm_slot2_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+    const Gemm2Plan pl = gemm_slot2_plan(m, n, k);
+    return pl.splits > 1 ? (pl.tiles - pl.t0) * pl.splits * int64_t(kTileFloats) * 4 : 0;
+}
+
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
-                             int64_t m, int64_t n, int64_t k, void* y, int y_f16,
-                             hipStream_t stream) {
+                             int64_t m, int64_t n, int64_t k, void* y, int y_f16, void* ws,
+                             int64_t ws_bytes, hipStream_t stream) {
     if (!gemm_slot2_fits(m, n, k)) return hipErrorInvalidValue;
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_slot2_kernel),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    const int64_t tiles_m = (m + BM - 1) / BM, tiles_n = (n + BN - 1) / BN;
-    const int64_t tiles = tiles_m * tiles_n;
-    const Plan pl = plan_split(tiles, int(k / 512), cu_count());
-    const int64_t items = (tiles - pl.t0) * pl.splits;
-    float* ws = nullptr;
-    if (pl.splits > 1) {
-        void* p = nullptr;
-        const hipError_t e = workspace(kWorkspacePartials, stream, size_t(items) * kTileFloats * sizeof(float), &p);
-        if (e != hipSuccess) return e;
-        ws = static_cast<float*>(p);
-    }
+    const Gemm2Plan pl = gemm_slot2_plan(m, n, k);
+    const int64_t items = (pl.tiles - pl.t0) * pl.splits;
+    if (pl.splits > 1 && (ws == nullptr || ws_bytes < items * int64_t(kTileFloats) * 4))
+        return hipErrorInvalidValue;
+    hipError_t e = allow_lds(reinterpret_cast<const void*>(gemm_slot2_kernel), kLds);
+    if (e != hipSuccess) return e;
+    const int64_t tiles_n = (n + BN - 1) / BN;
+    float* part = pl.splits > 1 ? static_cast<float*>(ws) : nullptr;
     const int64_t chunk_a = (pl.t0 + 7) / 8, chunk_b = (items + 7) / 8;
     hipLaunchKernelGGL(gemm_slot2_kernel, dim3(unsigned(8 * (chunk_a + chunk_b))), dim3(kThreads),
                        size_t(kLds), stream, packed, scales, x, m, n, k, y, y_f16, int(tiles_n),
-                       int(tiles), pl.t0, int(chunk_a), pl.splits, int(chunk_b), ws);
+                       int(pl.tiles), int(pl.t0), int(chunk_a), pl.splits, int(chunk_b), part);
     if (pl.splits > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(kRegs * (tiles - pl.t0))), dim3(kThreads), 0, stream,
-                           ws, m, n, y, y_f16, int(tiles_n), pl.t0, pl.splits);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(kRegs * (pl.tiles - pl.t0))),
+                           dim3(kThreads), 0, stream, part, m, n, y, y_f16, int(tiles_n),
+                           int(pl.t0), pl.splits);
     }
     return hipGetLastError();
 }

@@ -443,31 +443,14 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     }
 }
 
-int num_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
-    return cus;
-}
-
 template <int FL, bool ROT>
 hipError_t launch_fl(unsigned grid, size_t lds, const uint8_t* packed, const uint16_t* scales,
                      const uint16_t* x, const int8_t* signs, uint16_t* x_rot, int64_t n,
                      int64_t k, int rpc, void* y, int y_f16, hipStream_t stream) {
     const int base = int(n / grid), rem = int(n % grid);
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL, ROT>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsLimit));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL, ROT>), int(kLdsLimit));
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_m1_slot2_kernel<FL, ROT>), dim3(grid), dim3(kThreads), lds, stream,
                        packed, scales, x, signs, x_rot, k, base, rem, rpc, y, y_f16);
     return hipGetLastError();
@@ -482,7 +465,7 @@ struct M1Plan {
 
 M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     const int64_t nb = k / kBlock;
-    const int64_t grid = n < num_cus() ? n : num_cus();
+    const int64_t grid = n < cu_count() ? n : cu_count();
     const int64_t rows = (n + grid - 1) / grid;                  // largest slice
     int64_t rpc = kMaxSegsPerChunk / nb;
     if (rpc < 1) rpc = 1;
@@ -532,7 +515,7 @@ hipError_t launch_m1(const uint8_t* packed, const uint16_t* scales, const uint16
 
 bool m1_fits(int64_t m, int64_t n, int64_t k, bool rot) {
     const int64_t nb = k / kBlock;
-    const int64_t grid = n < num_cus() ? n : num_cus();
+    const int64_t grid = n < cu_count() ? n : cu_count();
     const int64_t rows = (n + grid - 1) / grid;
     // one image pass (32 threads per block, one half-wave per rotated block)
     // and 32-bit buffer offsets

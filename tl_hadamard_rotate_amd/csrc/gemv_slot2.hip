@@ -384,18 +384,6 @@ __global__ __launch_bounds__(64 * max_waves(NT)) void gemv_slot2_kernel(
     }
 }
 
-int num_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
-    return cus;
-}
-
 struct Plan {
     int64_t grid;
     int ksplit;
@@ -407,7 +395,7 @@ struct Plan {
 Plan make_plan(int64_t n, int max_w) {
     Plan p;
     const int64_t tiles = (n + 15) / 16;
-    p.grid = tiles < num_cus() ? tiles : num_cus();
+    p.grid = tiles < cu_count() ? tiles : cu_count();
     const int64_t rows_per_wg = (n + p.grid - 1) / p.grid;
     const int64_t tiles_per_wg = (rows_per_wg + 15) / 16;
     if (tiles_per_wg >= max_w) {
@@ -424,14 +412,9 @@ template <int NT, bool XLDS>
 hipError_t launch_one(const Plan& plan, const uint8_t* packed, const uint16_t* scales,
                       const uint16_t* x, int mt, int64_t n, int64_t k, void* y, int y_f16,
                       hipStream_t stream) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        const hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void*>(gemv_slot2_kernel<NT, XLDS>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, int(kLdsLimit));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    const hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(gemv_slot2_kernel<NT, XLDS>), int(kLdsLimit));
+    if (e != hipSuccess) return e;
     size_t lds = size_t(kLutBytes) + size_t(plan.waves) * NT * 2 * 64 * 4 +
                  (XLDS ? size_t(mt) * size_t(k) * 2 + 128 : 0);
     // ask for more than half of the CU's LDS so that two workgroups never share a CU

@@ -3,7 +3,9 @@
 // leaves every output untouched.
 #include <stdint.h>
 
+#include <initializer_list>
 #include <string>
+#include <utility>
 
 #include "../../include/tl.h"
 #include "tl_internal.h"
@@ -63,6 +65,18 @@ tl_status check_layer(const uint8_t* packed, const uint16_t* scales, int32_t fmt
     return TL_OK;
 }
 
+// workspace of a prefill product: present when needed, large enough, aligned,
+// and overlapping none of the call's buffers
+tl_status check_workspace(int64_t need, const void* ws, int64_t ws_bytes,
+                          std::initializer_list<std::pair<const void*, int64_t>> bufs) {
+    if (need == 0) return TL_OK;
+    if (!ws || ws_bytes < need) return TL_ERR_WORKSPACE;
+    if (!aligned16(ws)) return TL_ERR_ALIGN;
+    for (const auto& b : bufs)
+        if (b.first && overlap(ws, need, b.first, b.second)) return TL_ERR_ALIAS;
+    return TL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -118,27 +132,57 @@ tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t fmt, co
         tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
 }
 
+int64_t tl_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt) {
+    if (!layer_shape_ok(M, N, K) || !known_fmt(fmt) || !tl::gemm_fits(M, N, K)) return -1;
+    return tl::gemm_workspace_bytes(M, N, K, fmt, false);
+}
+
+tl_status tl_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t* out) {
+    if (!out) return TL_ERR_NULL;
+    if (!layer_shape_ok(M, N, K) || !tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;
+    const tl::Gemm2Plan p = tl::gemm_slot2_plan(M, N, K);
+    out[0] = p.tiles;
+    out[1] = p.t0;
+    out[2] = p.splits;
+    return TL_OK;
+}
+
 tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x_rot,
-                  int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype, hipStream_t stream) {
-    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+                  int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
+    tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
     if (st != TL_OK) return st;
-    return launched(
-        tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
+    if (!tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;
+    const int64_t need = tl::gemm_workspace_bytes(M, N, K, fmt, false);
+    st = check_workspace(need, workspace, workspace_bytes,
+                         {{packed, N * row_bytes(K, fmt)}, {scales, N * (K / TL_GROUP) * 2},
+                          {x_rot, M * K * 2}, {y, M * N * (y_dtype == TL_F32 ? 4 : 2)}});
+    if (st != TL_OK) return st;
+    return launched(tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16,
+                                    workspace, workspace_bytes, stream));
 }
 
 tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                        const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
-                       int32_t y_dtype, hipStream_t stream) {
-    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+                       int32_t y_dtype, void* workspace, int64_t workspace_bytes,
+                       hipStream_t stream) {
+    tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
     if (st != TL_OK) return st;
-    return launched(
-        tl::launch_gemm_bf16(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
+    if (!tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;
+    const int64_t need = tl::gemm_workspace_bytes(M, N, K, fmt, true);
+    st = check_workspace(need, workspace, workspace_bytes,
+                         {{packed, N * row_bytes(K, fmt)}, {scales, N * (K / TL_GROUP) * 2},
+                          {x_rot, M * K * 2}, {y, M * N * (y_dtype == TL_F32 ? 4 : 2)}});
+    if (st != TL_OK) return st;
+    return launched(tl::launch_gemm_bf16(packed, scales, fmt, x_rot, M, N, K, y,
+                                         y_dtype == TL_F16, workspace, workspace_bytes, stream));
 }
 
 tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x,
                     const int8_t* signs, int64_t M, int64_t N, int64_t K, uint16_t* x_rot, void* y,
-                    int32_t y_dtype, hipStream_t stream) {
-    const tl_status st = check_layer(packed, scales, fmt, x, M, N, K, y, y_dtype);
+                    int32_t y_dtype, void* workspace, int64_t workspace_bytes,
+                    hipStream_t stream) {
+    tl_status st = check_layer(packed, scales, fmt, x, M, N, K, y, y_dtype);
     if (st != TL_OK) return st;
     if (!signs || !x_rot) return TL_ERR_NULL;
     if (!aligned16(signs) || !aligned16(x_rot)) return TL_ERR_ALIGN;
@@ -148,6 +192,15 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
         overlap(x_rot, xb, scales, N * (K / TL_GROUP) * 2) || overlap(x_rot, xb, y, yb) ||
         overlap(y, yb, signs, K))
         return TL_ERR_ALIAS;
+    const bool prefill = M >= 64;
+    if (prefill) {
+        if (!tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;
+        st = check_workspace(tl::gemm_workspace_bytes(M, N, K, fmt, false), workspace,
+                             workspace_bytes,
+                             {{packed, N * row_bytes(K, fmt)}, {scales, N * (K / TL_GROUP) * 2},
+                              {x, xb}, {signs, K}, {x_rot, xb}, {y, yb}});
+        if (st != TL_OK) return st;
+    }
     const int y_f16 = y_dtype == TL_F16;
     if (fmt == TL_FMT_SLOT2 && tl::linear_m1_slot2_fits(M, N, K))
         return launched(
@@ -157,7 +210,8 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
             tl::launch_linear_m1_trit5(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
     hipError_t e = tl::launch_hadamard(x, signs, M, K, x_rot, stream);
     if (e != hipSuccess) return launched(e);
-    e = M >= 64 ? tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream)
+    e = prefill ? tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_f16, workspace,
+                                  workspace_bytes, stream)
                 : tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream);
     return launched(e);
 }
@@ -177,15 +231,6 @@ tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int64_t K,
     return launched(tl::launch_quantize(w, signs, N, K, codes, scales, stream));
 }
 
-tl_status tl_stream_read(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
-                         hipStream_t stream) {
-    if (!buf || !out) return TL_ERR_NULL;
-    if (bytes < 16 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return TL_ERR_SHAPE;
-    if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(out) & 3u)) return TL_ERR_ALIGN;
-    if (overlap(out, 65 * 4, buf, bytes)) return TL_ERR_ALIAS;
-    return launched(tl::launch_stream_read(buf, bytes, out, blocks, stream));
-}
-
 const char* tl_status_str(tl_status status) {
     switch (status) {
         case TL_OK: return "TL_OK";
@@ -196,6 +241,7 @@ const char* tl_status_str(tl_status status) {
         case TL_ERR_ALIAS: return "TL_ERR_ALIAS";
         case TL_ERR_LAUNCH: return "TL_ERR_LAUNCH";
         case TL_ERR_DTYPE: return "TL_ERR_DTYPE";
+        case TL_ERR_WORKSPACE: return "TL_ERR_WORKSPACE";
     }
     return "TL_ERR_UNKNOWN";
 }

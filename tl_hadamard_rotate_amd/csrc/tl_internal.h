@@ -11,6 +11,12 @@ constexpr int kBlock = 1024;        // Hadamard block width
 constexpr int kGroup = 128;         // weights per binary16 scale
 constexpr int kTrit5GroupBytes = 26;
 
+// Compute units of the current device (looked up once per device).
+int cu_count();
+// Let `kernel` use `bytes` of dynamic LDS on the current device (once per
+// kernel and device; thread-safe).
+hipError_t allow_lds(const void* kernel, int bytes);
+
 hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt,
                        uint8_t* packed, int32_t* bad_count, hipStream_t stream);
 hipError_t launch_unpack(const uint8_t* packed, int64_t n, int64_t k, int fmt,
@@ -43,10 +49,6 @@ hipError_t launch_linear_m1_trit5(const uint8_t* packed, const uint16_t* scales,
 hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                              hipStream_t stream);
-// Library-owned device workspace of `kind` for `stream` on the current
-// device, at least `bytes` long (grown with hipMalloc when needed).
-enum { kWorkspacePartials = 0, kWorkspaceSlot2 = 1 };
-hipError_t workspace(int kind, hipStream_t stream, size_t bytes, void** out);
 // The dense trit packing rewritten as 2-bit slots (same codes), row-major
 // [n][k/4] bytes.
 hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uint8_t* slot2,
@@ -59,24 +61,40 @@ hipError_t launch_gemv_bit1(const uint8_t* packed, const uint16_t* scales, const
                             int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                             hipStream_t stream);
 // Prefill GEMM of the 2-bit-slot packing with the weights decoded in
-// registers; usable when gemm_slot2_fits(m, n, k)
+// registers; usable when gemm_slot2_fits(m, n, k).  Its launch plan: `tiles`
+// output tiles, tiles [0, t0) computed whole, each later one split along K
+// into `splits` parts whose fp32 partial sums need workspace.
 bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
+struct Gemm2Plan {
+    int64_t tiles, t0;
+    int splits;
+};
+Gemm2Plan gemm_slot2_plan(int64_t m, int64_t n, int64_t k);
+int64_t gemm_slot2_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
-                             int64_t m, int64_t n, int64_t k, void* y, int y_f16,
-                             hipStream_t stream);
+                             int64_t m, int64_t n, int64_t k, void* y, int y_f16, void* ws,
+                             int64_t ws_bytes, hipStream_t stream);
+// The bfloat16-activation product of the 2-bit-slot packing
+hipError_t launch_gemm_bf16_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                  int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                                  hipStream_t stream);
 // Rotate real-valued weight rows and round them to ternary g128
 hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
                            int8_t* codes, uint16_t* scales, hipStream_t stream);
+// Prefill products (fp16 or bfloat16 activations) of any packing.  Dense
+// trits and 1-bit codes are first rewritten as 2-bit slots into the start of
+// the caller's workspace; the K-split partial sums follow at the next
+// 256-byte boundary.  gemm_workspace_bytes gives the bytes a call needs (0:
+// none); gemm_fits whether the shape is supported at all.
+bool gemm_fits(int64_t m, int64_t n, int64_t k);
+int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int fmt, bool bf16);
+hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
+                       const uint16_t* x, int64_t m, int64_t n, int64_t k,
+                       void* y, int y_f16, void* ws, int64_t ws_bytes, hipStream_t stream);
 // The product with bfloat16 activations: codes as bfloat16 -1/0/+1 on the
 // matrix cores, each group's fp32 sums times the binary16 scale
 hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
                             const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
-                            hipStream_t stream);
-// Measurement helper: streaming read of `bytes` (a multiple of 16) with `blocks` workgroups
-hipError_t launch_stream_read(const void* p, int64_t bytes, uint32_t* out, int blocks,
-                              hipStream_t stream);
-hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
-                       const uint16_t* x, int64_t m, int64_t n, int64_t k,
-                       void* y, int y_f16, hipStream_t stream);
+                            void* ws, int64_t ws_bytes, hipStream_t stream);
 
 }  // namespace tl
