@@ -169,6 +169,22 @@ TL_API tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t 
                   void* y, int32_t y_dtype, void* workspace, int64_t workspace_bytes,
                   hipStream_t stream);
 
+/* tl_gemm without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same operation, rules, kernels, launch plan and
+ * results (bit for bit) as tl_gemm; it calls no allocator.  Its workspace is
+ * a file-scope device array of TL_GEMM_NOALLOC_MAX_WORKSPACE bytes (96 MiB)
+ * that every GPU the library runs on holds until the process ends; a shape
+ * whose tl_gemm_workspace_bytes exceeds it returns TL_ERR_WORKSPACE (dense
+ * trits and 1-bit codes need N * K / 4 bytes for their rewrite, so N * K up
+ * to 2^27 weights).  All calls on one GPU share that array: calls that may
+ * run at the same time on one GPU (other streams, other threads) race and
+ * must not be issued; calls in order on one stream are safe. */
+#define TL_GEMM_NOALLOC_MAX_WORKSPACE (96 << 20)
+TL_API tl_status tl_gemm_noalloc(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                                 const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
+                                 void* y, int32_t y_dtype, hipStream_t stream);
+
 /* The whole layer on unrotated activations:
  *   x_rot = R(x)  (as tl_hadamard_rotate),   y = dequant(codes, scales) . x_rot
  * i.e. y[m, n] = sum_k R(x)[m, k] * code[n, k] * scales[n, k/128]: the

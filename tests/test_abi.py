@@ -215,6 +215,28 @@ def test_gemm_bf16_validation():
     assert _gemv(fn, yd=3) == 7
 
 
+def test_gemm_noalloc_validation():
+    """tl_gemm_noalloc: tl_gemm's argument checks, and shapes whose workspace
+    exceeds its fixed scratch array are refused before any launch."""
+    f = tl.lib().tl_gemm_noalloc
+    P, S, X, Y = A, A + (1 << 32), A + (2 << 32), A + (3 << 32)
+
+    def call(packed=P, scales=S, fmt=0, x=X, m=64, n=1024, k=1024, y=Y, yd=0):
+        return f(packed, scales, fmt, x, m, n, k, y, yd, NULL)
+
+    assert call(packed=NULL) == 1
+    assert call(k=1000) == 2
+    assert call(fmt=5) == 3
+    assert call(x=X + 2) == 4
+    assert call(y=X) == 5
+    assert call(yd=4) == 7
+    limit = 96 << 20
+    n, k = 65536, 8192                  # 2-bit-slot rewrite of 128 MiB
+    assert tl.lib().tl_gemm_workspace_bytes(64, n, k, 0) > limit
+    assert call(fmt=0, n=n, k=k) == 8
+    assert call(fmt=2, n=n, k=k) == 8
+
+
 def test_layer_library_exports_no_probe():
     """The benchmark's read-only probe lives in its own library."""
     lib = ctypes.CDLL(tl.LIB_PATH)

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "tl_hadamard_rotate": (i32, [p, p, i64, i64, p, p]),
             "tl_gemv": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p, i64, p]),
+            "tl_gemm_noalloc": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_gemm_workspace_bytes": (i64, [i64, i64, i64, i32]),
             "tl_gemm_plan": (i32, [i64, i64, i64, p]),
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p, i64, p]),
@@ -215,7 +216,7 @@ def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch
             raise ValueError("out must be [M, N]")
     yd = TL_F32 if out_dtype == torch.float32 else TL_F16
     fn = getattr(lib(), call)
-    if call == "tl_gemv":
+    if call in ("tl_gemv", "tl_gemm_noalloc"):
         _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
                         _stream(x_rot)))
     else:
@@ -228,6 +229,13 @@ def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch
 def gemv(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
     """y[M, N] = x_rot . dequant(codes, scales)^T, decode-shaped (M <= 16)."""
     return _linear("tl_gemv", packed, scales, fmt, x_rot, out_dtype, out)
+
+
+def gemm_noalloc(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) -> torch.Tensor:
+    """``gemm`` through tl_gemm_noalloc: no workspace argument and no
+    allocation by the library (its workspace is a fixed device array of
+    TL_GEMM_NOALLOC_MAX_WORKSPACE bytes shared by all calls on a GPU)."""
+    return _linear("tl_gemm_noalloc", packed, scales, fmt, x_rot, out_dtype, out)
 
 
 def gemm_bf16(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None,

@@ -162,6 +162,22 @@ tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, co
                                     workspace, workspace_bytes, stream));
 }
 
+tl_status tl_gemm_noalloc(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
+                          const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
+                          int32_t y_dtype, hipStream_t stream) {
+    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    if (!tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;
+    const int64_t need = tl::gemm_workspace_bytes(M, N, K, fmt, false);
+    if (need > int64_t(TL_GEMM_NOALLOC_MAX_WORKSPACE)) return TL_ERR_WORKSPACE;
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
+    const hipError_t e = tl::noalloc_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return launched(e);
+    return launched(tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, ws,
+                                    ws_bytes, stream));
+}
+
 tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                        const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
                        int32_t y_dtype, void* workspace, int64_t workspace_bytes,

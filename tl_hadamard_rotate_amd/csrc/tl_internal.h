@@ -96,5 +96,8 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
 hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
                             const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                             void* ws, int64_t ws_bytes, hipStream_t stream);
+// Device address and size of the current device's copy of the file-scope
+// workspace of tl_gemm_noalloc (looked up once per device; thread-safe).
+hipError_t noalloc_scratch(void** out, int64_t* bytes);
 
 }  // namespace tl
