@@ -209,6 +209,62 @@ TL_API tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_
                     uint16_t* x_rot, void* y, int32_t y_dtype, void* workspace,
                     int64_t workspace_bytes, hipStream_t stream);
 
+/* One linear of a decode chain (tl_linear_chain): the arguments of tl_linear
+ * at M = 1.  packed: TL_FMT_SLOT2 codes [N, K/4]; scales [N, K/128]; x: the
+ * unrotated binary16 input [K], either ready when the chain starts or lying
+ * within the binary16 y of an earlier linear of the chain; signs [K]; x_rot: [K]
+ * binary16 receiving R(x), or NULL; y: [N] of y_dtype. */
+typedef struct {
+    const uint8_t* packed;
+    const uint16_t* scales;
+    const uint16_t* x;
+    const int8_t* signs;
+    uint16_t* x_rot;
+    void* y;
+    int64_t N;
+    int64_t K;
+    int32_t fmt;
+    int32_t y_dtype;
+} tl_chain_op;
+
+/* Bytes of the encoded plan and of the sync buffer of a chain of `count`
+ * linears (1 <= count <= 65536; -1 otherwise).  Host only. */
+TL_API int64_t tl_chain_plan_bytes(int32_t count);
+TL_API int64_t tl_chain_sync_bytes(int32_t count);
+
+/* Check a chain and encode its plan into `plan` (HOST memory of plan_bytes
+ * >= tl_chain_plan_bytes(count) bytes), which the caller copies to device
+ * memory once and may launch any number of times.  Rules: fmt TL_FMT_SLOT2;
+ * 1 <= N <= 2^24; K % 1024 == 0, 1024 <= K <= 32768, with each workgroup's
+ * share of the rows (ceil(N / CUs)) times K/1024 at most 2048 and its LDS
+ * within one CU (TL_ERR_SHAPE); every pointer 16-byte aligned.  An output (y,
+ * x_rot) may overlap nothing else of the chain except that the x of a later
+ * linear may lie within a binary16 y, and that linear then waits for the whole
+ * y to be written (else TL_ERR_ALIAS).  The plan records the
+ * compute-unit count of the current device and is valid only there.  Bytes
+ * 12..15 of the plan (uint32) hold the number of polls after which a wait for
+ * an input gives up (set by the encoder; a smaller value only makes a failure
+ * show sooner). */
+TL_API tl_status tl_chain_encode(const tl_chain_op* ops, int32_t count, void* plan,
+                                 int64_t plan_bytes);
+
+/* Run an encoded chain in one launch: each linear is tl_linear at M = 1 (the
+ * same results, bit for bit), in order, with the next linear's weight stream
+ * starting before the current one has finished, so the stream does not stop
+ * at linear boundaries (the rotation still runs on every linear's input:
+ * Persian page, paragraph 3).  plan: device copy of tl_chain_encode's
+ * output; sync: device uint32 [tl_chain_sync_bytes(count) / 4], all zero
+ * before the first call, not overlapping plan; every completed call leaves it
+ * as it found it except word count + 1, the error word, which a failure sets
+ * (first failure kept) and only the caller clears: 1 = the plan does not
+ * match count or the device, 2 + i = linear i's wait for its input gave up
+ * (its input was not complete within the plan's poll limit: the GPU must not
+ * be shared with other work while a chain with such waits runs).  After a
+ * failure the outputs are unspecified.  Calls sharing a sync buffer must not
+ * run at the same time. */
+TL_API tl_status tl_linear_chain(const void* plan, int32_t count, uint32_t* sync,
+                                 hipStream_t stream);
+
 /* The prefill product with bfloat16 rotated activations:
  *   y[m, n] = sum_g S[n, g] * sum_{k in g} code[n, k] * x_rot[m, k]
  * with the codes entering the matrix cores as exact bfloat16 -1/0/+1 and each

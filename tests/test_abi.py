@@ -4,6 +4,7 @@ launch.  Every call here fails validation, so nothing touches a device."""
 import ctypes
 import os
 import re
+import struct
 
 import pytest
 
@@ -252,3 +253,69 @@ def test_probe_library_validation():
     assert f(A, 1024, A + 0x100000, 0, NULL) == 1
     assert f(A + 8, 1024, A + 0x100000, 4, NULL) == 1
     assert f(A, 1024, A + 16, 4, NULL) == 1
+
+
+def _chain_encode(ops):
+    L = tl.lib()
+    arr = (tl.ChainOp * len(ops))(*ops)
+    nbytes = L.tl_chain_plan_bytes(len(ops))
+    host = (ctypes.c_uint8 * max(nbytes, 1))()
+    return L.tl_chain_encode(arr, len(ops), host, nbytes), bytes(host)
+
+
+def _op(base, n=1024, k=1024, y=None, x=None, yd=1, fmt=1, x_rot=0):
+    """A chain linear on fake, far-apart addresses below `base`."""
+    return tl.ChainOp(base, base + (1 << 28), x if x is not None else base + (2 << 28),
+                      base + (3 << 28), x_rot, y if y is not None else base + (4 << 28), n, k, fmt, yd)
+
+
+def test_chain_sizes():
+    L = tl.lib()
+    assert L.tl_chain_plan_bytes(1) == 128 and L.tl_chain_plan_bytes(448) == 64 * 449
+    assert L.tl_chain_sync_bytes(1) == 16 and L.tl_chain_sync_bytes(448) == 1808   # 4 * 450, to 16
+    for bad in (0, -1, 65537):
+        assert L.tl_chain_plan_bytes(bad) == -1 and L.tl_chain_sync_bytes(bad) == -1
+
+
+def test_chain_encode_validation():
+    B0, B1, B2 = A, A + (8 << 28), A + (16 << 28)
+    # a valid two-linear chain whose second input is the first output
+    y0 = B0 + (4 << 28)
+    st, plan = _chain_encode([_op(B0, n=1024, k=1024), _op(B1, n=512, k=1024, x=y0)])
+    assert st == 0
+    magic, count, grid, polls = struct.unpack_from("<IiiI", plan, 0)
+    assert count == 2 and grid > 0 and polls > 0
+    # per linear: 6 pointers, n, k, the producer of its input, binary16 output
+    n1, k1, dep1, f16 = struct.unpack_from("<iiii", plan, 64 + 64 + 48)
+    assert (n1, k1, dep1, f16) == (512, 1024, 0, 1)
+    assert struct.unpack_from("<i", plan, 64 + 48 + 8)[0] == -1
+    # x within a larger binary16 y (q inside q|k|v): a dependency too
+    st, plan = _chain_encode([_op(B0, n=8192, k=5120), _op(B1, n=5120, k=6144, x=y0 + 2048)])
+    assert st == 0 and struct.unpack_from("<i", plan, 64 + 64 + 56)[0] == 0
+    # NULL, format, dtype, shape, alignment
+    assert _chain_encode([_op(B0, y=0)])[0] == 1
+    assert _chain_encode([_op(B0, fmt=0)])[0] == 3
+    assert _chain_encode([_op(B0, yd=5)])[0] == 7
+    assert _chain_encode([_op(B0, k=1000)])[0] == 2
+    assert _chain_encode([_op(B0, k=33 * 1024)])[0] == 2
+    assert _chain_encode([_op(B0, n=1 << 25)])[0] == 2
+    assert _chain_encode([_op(B0, n=17408 * 8, k=17408)])[0] == 2   # one chunk per workgroup
+    assert _chain_encode([_op(B0, x_rot=B2 + 8)])[0] == 4
+    # a float32 y cannot feed a later linear; an input may not straddle a y;
+    # a later output may not overwrite an earlier input; outputs may not overlap
+    assert _chain_encode([_op(B0, yd=0), _op(B1, x=y0)])[0] == 5
+    assert _chain_encode([_op(B0, n=1024), _op(B1, k=1024, x=y0 + 1024)])[0] == 5
+    assert _chain_encode([_op(B0), _op(B1, y=B0 + (2 << 28))])[0] == 5
+    assert _chain_encode([_op(B0), _op(B1, y=y0 + 16)])[0] == 5
+    assert _chain_encode([_op(B0, x_rot=y0)])[0] == 5
+    # a linear cannot read its own output
+    assert _chain_encode([_op(B0, x=y0)])[0] == 5
+
+
+def test_chain_launch_validation():
+    f = tl.lib().tl_linear_chain
+    assert f(NULL, 1, A, NULL) == 1
+    assert f(A, 1, NULL, NULL) == 1
+    assert f(A, 0, A + 0x100000, NULL) == 2
+    assert f(A + 8, 1, A + 0x100000, NULL) == 4
+    assert f(A, 1, A + 64, NULL) == 5          # sync inside the plan

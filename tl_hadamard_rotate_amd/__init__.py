@@ -64,6 +64,10 @@ def lib() -> ctypes.CDLL:
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p, i64, p]),
             "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
             "tl_gemm_bf16": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p, i64, p]),
+            "tl_chain_plan_bytes": (i64, [i32]),
+            "tl_chain_sync_bytes": (i64, [i32]),
+            "tl_chain_encode": (i32, [p, i32, p, i64]),
+            "tl_linear_chain": (i32, [p, i32, p, p]),
             "tl_status_str": (ctypes.c_char_p, [i32]),
             "tl_last_error": (ctypes.c_char_p, []),
         }
@@ -313,3 +317,69 @@ class TernaryLinear:
         return linear(self.packed, self.scales, self.fmt, x, self.signs, out_dtype)
 
     __call__ = forward
+
+
+class ChainOp(ctypes.Structure):
+    """tl_chain_op of include/tl.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("x", ctypes.c_void_p),
+                ("signs", ctypes.c_void_p), ("x_rot", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("fmt", ctypes.c_int32),
+                ("y_dtype", ctypes.c_int32)]
+
+
+class Chain:
+    """A decode chain (tl_linear_chain): linears at M = 1 run in order in one
+    launch, each the rotation of its input and the ternary product, with the
+    next linear's weights requested before the current one ends.  ``ops``:
+    dicts with packed, scales, fmt, x, signs, y and optionally x_rot (device
+    tensors; x [1, K] or [K] binary16, y [1, N] or [N] float32/float16).  An
+    x that is a view into the binary16 y of an earlier op makes that op wait
+    for it.  The plan is encoded once (on the host, by the library) and kept
+    on the device with the sync buffer; the tensors must stay alive."""
+
+    def __init__(self, ops):
+        if not ops:
+            raise ValueError("a chain needs at least one linear")
+        count = len(ops)
+        arr = (ChainOp * count)()
+        for i, o in enumerate(ops):
+            _need(o["packed"], "packed", torch.uint8, 2)
+            _need(o["scales"], "scales", torch.float16, 2)
+            _need(o["x"], "x", torch.float16)
+            _need(o["signs"], "signs", torch.int8, 1)
+            n, k = o["packed"].shape[0], o["x"].numel()
+            y = o["y"]
+            if y.dtype not in (torch.float32, torch.float16) or y.numel() != n or not y.is_contiguous():
+                raise ValueError("y must be a contiguous float32/float16 tensor of N elements")
+            if o["signs"].numel() != k or o["scales"].shape != (n, k // GROUP):
+                raise ValueError("signs must have K entries and scales be [N, K/128]")
+            if o["packed"].numel() != packed_bytes(n, k, o["fmt"]):
+                raise ValueError("packed size does not match N, K and the format")
+            xr = o.get("x_rot")
+            if xr is not None:
+                _need(xr, "x_rot", torch.float16)
+            arr[i] = ChainOp(o["packed"].data_ptr(), o["scales"].data_ptr(), o["x"].data_ptr(),
+                             o["signs"].data_ptr(), 0 if xr is None else xr.data_ptr(),
+                             y.data_ptr(), n, k, o["fmt"],
+                             TL_F32 if y.dtype == torch.float32 else TL_F16)
+        L = lib()
+        nbytes = int(L.tl_chain_plan_bytes(count))
+        host = (ctypes.c_uint8 * nbytes)()
+        _check("tl_chain_encode", L.tl_chain_encode(arr, count, host, nbytes))
+        device = ops[0]["x"].device
+        self.count = count
+        self.plan = torch.frombuffer(bytearray(host), dtype=torch.uint8).to(device)
+        self.sync = torch.zeros(int(L.tl_chain_sync_bytes(count)) // 4, dtype=torch.int32,
+                                device=device)
+        self._ops = ops
+
+    def __call__(self) -> None:
+        _check("tl_linear_chain", lib().tl_linear_chain(_ptr(self.plan), self.count,
+                                                        _ptr(self.sync), _stream(self.sync)))
+
+    def error(self) -> int:
+        """The chain's error word (0: none; see tl_linear_chain)."""
+        return int(self.sync[self.count + 1].item())
+
+    def clear_error(self) -> None:
+        self.sync[self.count + 1].zero_()

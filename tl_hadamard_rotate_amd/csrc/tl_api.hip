@@ -7,7 +7,6 @@
 #include <string>
 #include <utility>
 
-#include "../../include/tl.h"
 #include "tl_internal.h"
 
 namespace {
@@ -16,6 +15,7 @@ thread_local std::string g_last_error;
 
 constexpr int64_t kMaxRows = int64_t(1) << 24;     // M and N
 constexpr int64_t kMaxElems = int64_t(1) << 36;    // M*K, N*K and M*N
+constexpr int32_t kMaxChain = 65536;               // linears in one chain
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -230,6 +230,30 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
                                   workspace_bytes, stream)
                 : tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_f16, stream);
     return launched(e);
+}
+
+int64_t tl_chain_plan_bytes(int32_t count) {
+    return count >= 1 && count <= kMaxChain ? tl::chain_plan_bytes(count) : -1;
+}
+
+int64_t tl_chain_sync_bytes(int32_t count) {
+    return count >= 1 && count <= kMaxChain ? tl::chain_sync_bytes(count) : -1;
+}
+
+tl_status tl_chain_encode(const tl_chain_op* ops, int32_t count, void* plan, int64_t plan_bytes) {
+    if (!ops || !plan) return TL_ERR_NULL;
+    if (count < 1 || count > kMaxChain || plan_bytes < tl::chain_plan_bytes(count))
+        return TL_ERR_SHAPE;
+    return static_cast<tl_status>(tl::chain_encode(ops, count, plan));
+}
+
+tl_status tl_linear_chain(const void* plan, int32_t count, uint32_t* sync, hipStream_t stream) {
+    if (!plan || !sync) return TL_ERR_NULL;
+    if (count < 1 || count > kMaxChain) return TL_ERR_SHAPE;
+    if (!aligned16(plan) || !aligned16(sync)) return TL_ERR_ALIGN;
+    if (overlap(plan, tl::chain_plan_bytes(count), sync, tl::chain_sync_bytes(count)))
+        return TL_ERR_ALIAS;
+    return launched(tl::launch_chain(plan, count, sync, stream));
 }
 
 tl_status tl_quantize(const float* w, const int8_t* signs, int64_t N, int64_t K, int8_t* codes,

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/tl.h"
+
 namespace tl {
 
 constexpr int kBlock = 1024;        // Hadamard block width
@@ -96,6 +98,12 @@ hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
 hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
                             const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                             void* ws, int64_t ws_bytes, hipStream_t stream);
+// Decode chains (tl_linear_chain): plan and sync-buffer sizes, the host-side
+// check and encoding of a chain (a tl_status), and the launch.
+int64_t chain_plan_bytes(int64_t count);
+int64_t chain_sync_bytes(int64_t count);
+int chain_encode(const tl_chain_op* ops, int32_t count, void* plan_out);
+hipError_t launch_chain(const void* plan, int32_t count, uint32_t* sync, hipStream_t stream);
 // Device address and size of the current device's copy of the file-scope
 // workspace of tl_gemm_noalloc (looked up once per device; thread-safe).
 hipError_t noalloc_scratch(void** out, int64_t* bytes);
