@@ -1,11 +1,14 @@
 """Benchmark of the ternary g128 decode path on one MI355X.
 
 A step is one decode pass (M = 1) over the 27B-class MLP projections
-gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120): for
-each projection the signed 1024-block Hadamard rotation of its input and the
-ternary product (tl_linear: one fused kernel per projection with either
-packing).  Inputs are seeded synthetic tensors with the workload's
-distributions.
+gate (K=5120, N=17408), up (K=5120, N=17408) and down (K=17408, N=5120):
+two tl_linear launches, gate|up (rows concatenated: the input rotated once
+with the signed 1024-block Hadamard transform, binary16 output) then down,
+whose input is the gate part of that output (the SwiGLU between them in a
+model is outside the library).  Each launch is the fused rotation + ternary
+product kernel.  Inputs are seeded synthetic tensors with the workload's
+distributions.  With --fmt trit5 the step is the three projections as
+separate tl_linear launches.
 
 Timing.  Each step is captured once in a HIP graph; the weights are replicated
 into --copies distinct buffers (one graph per copy) and the timed loop cycles
@@ -13,18 +16,24 @@ through them, so no step finds its weights in the 256 MB last-level cache.
 W warm-up steps, then exactly K timed steps between two HIP events on the
 launch stream, with a device synchronisation on both sides.
 
-Dominant kernel (roofline): the fused tl_linear kernel, whose three launches
-make up the step; average launch time between HIP events on the launch
-stream.  HBM traffic comes from the rocprofv3 counter summary under
-profiles/ and is reported only while the kernel source is the one those
-counters were taken from.
+Dominant kernel (roofline): the fused rotate + GEMV kernel, two launches
+per step; its average launch duration comes from HIP events recorded on the
+launch stream between consecutive launches, enqueued behind a GPU sleep so
+that host submission is not counted (the step-timed figure per launch is
+reported beside it, and the rocprofv3 kernel-trace average from profiles/
+when the summary matches the kernel source).  HBM
+traffic comes from the rocprofv3 counter summary under profiles/ and is
+reported only while the kernel source is the one those counters were taken
+from.
 
-Extras: the other packing, the prefill GEMM sweep (and its bfloat16 variant
-at M = 4096), batched decode over the attention projections, the rotation
-at prefill size, the 64-layer weight
-stream (one rotation per linear, and one per input with q|k|v and gate|up
-concatenated), the weight quantiser, the decode step with 1-bit weights, and
-the CPU oracle on a bounded sample.
+Extras: each launch of the step, the step as one tl_linear_chain launch,
+the three projections as separate launches (and the GEMVs alone), the other
+packing, the 64-layer weight stream (one chain launch per token with
+dependent and with independent inputs, and one launch per linear or per
+input), the prefill GEMM sweep (and its bfloat16 variant at M = 4096),
+batched decode over the attention projections, the rotation at prefill size,
+the weight quantiser, the decode step with 1-bit weights, and the CPU oracle
+on a bounded sample.
 
 Prints one JSON line on stdout; progress goes to stderr.
     python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--fmt slot2|trit5]
@@ -52,6 +61,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 STEP_LINEARS = ("gate", "up", "down")
 FMT_NAMES = {"trit5": 0, "slot2": 1, "bit1": 2}
 KERNEL_SRC = {0: "gemv_trit5.hip", 1: "gemv_m1.hip"}
+PROFILE_NAME = {0: "linear_m1_trit5_decode_mlp", 1: "linear_m1_slot2_decode_step"}
 
 
 def log(msg: str) -> None:
@@ -85,14 +95,14 @@ def rotate_bytes(m: int, k: int) -> int:
 def source_sha(fmt: int) -> str:
     """First 16 hex digits of the SHA-256 of the kernel's source file followed
     by the kernel headers it includes, in the order of its #include lines
-    (tl_internal.h, the library's declarations, is left out)."""
+    (tl_internal.h and tl.h, the library's declarations, are left out)."""
     csrc = os.path.join(ROOT, "tl_hadamard_rotate_amd", "csrc")
     with open(os.path.join(csrc, KERNEL_SRC[fmt]), "rb") as f:
         data = f.read()
     h = hashlib.sha256(data)
     for name in re.findall(rb'^#include "([^"]+)"', data, re.M):
         path = os.path.join(csrc, name.decode())
-        if name != b"tl_internal.h" and os.path.exists(path):
+        if name not in (b"tl_internal.h", b"../../include/tl.h") and os.path.exists(path):
             with open(path, "rb") as f:
                 h.update(f.read())
     return h.hexdigest()[:16]
@@ -101,8 +111,7 @@ def source_sha(fmt: int) -> str:
 def traffic_from_profiles(fmt: int):
     """HBM bytes per GEMV launch from the committed counter summary, or None
     when there is none for the current kernel source."""
-    name = "linear_m1_slot2" if fmt == 1 else "linear_m1_trit5"
-    path = os.path.join(ROOT, "profiles", f"{name}_decode_mlp_pmc.txt")
+    path = os.path.join(ROOT, "profiles", f"{PROFILE_NAME[fmt]}_pmc.txt")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -111,6 +120,21 @@ def traffic_from_profiles(fmt: int):
     if not sha or not val or sha.group(1) != source_sha(fmt):
         return None
     return float(val.group(1))
+
+
+def rocprof_launch_us(fmt: int):
+    """Average duration (us) of the step's kernel in the committed rocprofv3
+    kernel-trace summary, or None when there is none for the current kernel
+    source."""
+    path = os.path.join(ROOT, "profiles", f"{PROFILE_NAME[fmt]}_trace.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256_16:\s*(\S+)", text, re.M)
+    val = re.search(r"^step_kernel_avg_ns:\s*([0-9.eE+]+)", text, re.M)
+    if not sha or not val or sha.group(1) != source_sha(fmt):
+        return None
+    return round(float(val.group(1)) / 1e3, 3)
 
 
 def build_step_inputs(torch, tl, synth, dev, fmt: int, copies: int):
@@ -176,35 +200,51 @@ def timed_replays(torch, graphs, count, warmup, stream):
     return start.elapsed_time(end)
 
 
-def cpu_baseline(oracle, synth, fmt, budget_s=12.0, rows=512):
+def cpu_baseline(oracle, synth, fmt, budget_s=8.0, rows=512):
     """The oracle as it stands, timed on the host on a bounded sample: the
     rotation plus unpack, dequantisation and fp64 matrix-vector product of the
-    first `rows` rows of gate, up and down.  Reported in GB/s of the same
-    algorithmic bytes as the GPU figure."""
+    first `rows` rows of gate, up and down (the step's projections), in GB/s
+    of the same algorithmic bytes as the GPU figure; once with the BLAS
+    thread pool as it is (the threads the oracle actually uses: `cores`) and
+    once limited to one thread."""
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        threadpool_limits, threads = None, os.cpu_count() or 1
     samples = []
     for name in STEP_LINEARS:
         k, n = synth.SHAPES[name]
         inp = synth.linear_inputs(rows, k, 1, seed=0, cfg=2, layer=0, linear=synth.LINEAR_ID[name])
         samples.append((inp, oracle.pack(inp.codes, fmt), k))
-    done, t0, passes = 0, time.perf_counter(), 0
-    while True:
-        for inp, packed, k in samples:
-            x_rot = oracle.rotate(inp.x, inp.signs)
-            oracle.matvec_packed(packed, inp.scales, fmt, x_rot, k)
-            done += gemv_bytes(rows, k, 1, fmt) + rotate_bytes(1, k)
-        passes += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(done / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"first {rows} rows of gate, up and down at M=1 (rotation + unpack + "
-                      f"fp64 dequantised matrix-vector product), {passes} passes in {dt:.1f} s"}
+
+    def rate():
+        done, t0, passes = 0, time.perf_counter(), 0
+        while True:
+            for inp, packed, k in samples:
+                x_rot = oracle.rotate(inp.x, inp.signs)
+                oracle.matvec_packed(packed, inp.scales, fmt, x_rot, k)
+                done += gemv_bytes(rows, k, 1, fmt) + rotate_bytes(1, k)
+            passes += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return done / dt / 1e9, passes, dt
+
+    v_all, passes, dt = rate()
+    v_one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            v_one = rate()[0]
+    cpu = host_cpu()
+    return {"value": round(v_all, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} rows of gate, up and down at M=1 (rotation + unpack + fp64 "
+                      f"dequantised matrix-vector product), {passes} passes in {dt:.1f} s with "
+                      f"the BLAS pool of {threads} threads; the rate of the sample, not an "
+                      f"extrapolation of a larger run",
+            "value_one_thread": None if v_one is None else round(v_one, 4),
+            "cpu_model": cpu["model"], "logical_cpus": cpu["logical_cpus"],
+            "usable_cpus": cpu["usable_cpus"]}
 
 
 def _event_time(torch, fn, reps):
@@ -532,14 +572,23 @@ def read_floor(torch, tl, dev, reps=20) -> int:
 
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
-    256 MiB written per launch), then 10 eager decode steps (per projection
-    tl_linear, and tl_gemv alone), weights cycled over 8 copies."""
+    256 MiB written per launch), then, with 2-bit slots, 10 eager steps (the
+    timed step: tl_linear on gate|up, then on down), then 10 eager decode
+    steps as separate launches per projection (tl_linear, and tl_gemv alone);
+    weights cycled over 8 copies."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+    if fmt == 1:
+        steps, _ = build_mlp_step(torch, tl, synth, dev, 8)
+        for i in range(10):
+            for fn in steps[i % 8]:
+                fn()
+        torch.cuda.synchronize()
+        del steps
     lins = build_step_inputs(torch, tl, synth, dev, fmt, 8)
     for lin in lins:
         tl.hadamard_rotate(lin["x"], lin["signs"], out=lin["x_rot"])
@@ -637,6 +686,221 @@ def profile_batched(torch, tl, synth, dev) -> int:
     return 0
 
 
+def chain_op_bytes(n: int, k: int, y_elem: int, fmt: int = 1, x_rot: bool = False) -> int:
+    """Algorithmic bytes of one linear of a decode chain: codes + scales, the
+    unrotated binary16 input and the int8 signs read, the output (y_elem
+    bytes per element) written, and the rotated input when it is kept."""
+    return (code_bytes(n, k, fmt) + n * (k // 128) * 2 + 2 * k + k + n * y_elem +
+            (2 * k if x_rot else 0))
+
+
+def build_chain_step(torch, tl, synth, dev, copies):
+    """The decode step as one tl_linear_chain launch per weight copy: gate|up
+    (the two projections that read the same input, rows concatenated: one
+    rotation) then down, whose input is the gate part of gate|up's binary16
+    output (the SwiGLU between them in a model is outside this library).
+    Returns the chains and the step's algorithmic bytes."""
+    import numpy as np
+
+    ins = {}
+    for name in STEP_LINEARS:
+        k, n = synth.SHAPES[name]
+        ins[name] = synth.linear_inputs(n, k, 1, seed=0, cfg=2, layer=0,
+                                        linear=synth.LINEAR_ID[name])
+    g, u, d = ins["gate"], ins["up"], ins["down"]
+    kg, ng = synth.SHAPES["gate"]
+    kd, nd = synth.SHAPES["down"]
+    gu_packed = tl.pack(torch.from_numpy(np.concatenate([g.codes, u.codes])).to(dev), 1)
+    gu_scales = torch.from_numpy(np.concatenate([g.scales, u.scales])).to(dev)
+    dn_packed = tl.pack(torch.from_numpy(d.codes).to(dev), 1)
+    dn_scales = torch.from_numpy(d.scales).to(dev)
+    x = torch.from_numpy(g.x).to(dev).view(-1)
+    s_gu, s_dn = torch.from_numpy(g.signs).to(dev), torch.from_numpy(d.signs).to(dev)
+    y_gu = torch.empty(2 * ng, dtype=torch.float16, device=dev)
+    y_dn = torch.empty(nd, dtype=torch.float32, device=dev)
+    chains = []
+    for c in range(copies):
+        pg, sg = (gu_packed, gu_scales) if c == 0 else (gu_packed.clone(), gu_scales.clone())
+        pd, sd = (dn_packed, dn_scales) if c == 0 else (dn_packed.clone(), dn_scales.clone())
+        chains.append(tl.Chain([dict(packed=pg, scales=sg, fmt=1, x=x, signs=s_gu, y=y_gu),
+                                dict(packed=pd, scales=sd, fmt=1, x=y_gu[:kd], signs=s_dn,
+                                     y=y_dn)]))
+    step_bytes = chain_op_bytes(2 * ng, kg, 2) + chain_op_bytes(nd, kd, 4)
+    return chains, step_bytes
+
+
+def build_mlp_step(torch, tl, synth, dev, copies):
+    """The decode step as two tl_linear launches per weight copy: gate|up (the
+    two projections that read the same input, rows concatenated: one rotation,
+    binary16 output) then down on the gate part of that output (the SwiGLU
+    between them in a model is outside this library; stream order makes down
+    wait for gate|up).  Returns per-copy lists of the two launches (callables)
+    and the step's algorithmic bytes."""
+    import numpy as np
+
+    ins = {}
+    for name in STEP_LINEARS:
+        k, n = synth.SHAPES[name]
+        ins[name] = synth.linear_inputs(n, k, 1, seed=0, cfg=2, layer=0,
+                                        linear=synth.LINEAR_ID[name])
+    g, u, d = ins["gate"], ins["up"], ins["down"]
+    kg, ng = synth.SHAPES["gate"]
+    kd, nd = synth.SHAPES["down"]
+    gu_packed = tl.pack(torch.from_numpy(np.concatenate([g.codes, u.codes])).to(dev), 1)
+    gu_scales = torch.from_numpy(np.concatenate([g.scales, u.scales])).to(dev)
+    dn_packed = tl.pack(torch.from_numpy(d.codes).to(dev), 1)
+    dn_scales = torch.from_numpy(d.scales).to(dev)
+    x = torch.from_numpy(g.x).to(dev)
+    s_gu, s_dn = torch.from_numpy(g.signs).to(dev), torch.from_numpy(d.signs).to(dev)
+    y_gu = torch.empty((1, 2 * ng), dtype=torch.float16, device=dev)
+    y_dn = torch.empty((1, nd), dtype=torch.float32, device=dev)
+    xr_gu = torch.empty((1, kg), dtype=torch.float16, device=dev)
+    xr_dn = torch.empty((1, kd), dtype=torch.float16, device=dev)
+    x_dn = y_gu[:, :kd]
+    steps = []
+    for c in range(copies):
+        pg, sg = (gu_packed, gu_scales) if c == 0 else (gu_packed.clone(), gu_scales.clone())
+        pd, sd = (dn_packed, dn_scales) if c == 0 else (dn_packed.clone(), dn_scales.clone())
+        steps.append([
+            (lambda pg=pg, sg=sg: tl.linear(pg, sg, 1, x, s_gu, out_dtype=torch.float16, out=y_gu,
+                                            x_rot=xr_gu)),
+            (lambda pd=pd, sd=sd: tl.linear(pd, sd, 1, x_dn, s_dn, out=y_dn, x_rot=xr_dn))])
+    launch_bytes = [linear_bytes(2 * ng, kg, 1, 1) - 2 * ng * 2,    # binary16 output
+                    linear_bytes(nd, kd, 1, 1)]
+    return steps, launch_bytes
+
+
+def per_launch_times_us(torch, steps, reps, stream):
+    """Average duration of each launch of a step, measured with HIP events
+    recorded on the launch stream between consecutive launches; everything is
+    enqueued behind a GPU sleep, so that the time between two events is the
+    launch's dispatch and execution, not the host's submission."""
+    import statistics
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        torch.cuda._sleep(100_000_000)
+        rows = []
+        for r in range(reps):
+            row = [torch.cuda.Event(enable_timing=True)]
+            row[0].record(stream)
+            for fn in steps[r % len(steps)]:
+                fn()
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                row.append(e)
+            rows.append(row)
+        torch.cuda.synchronize()
+    n = len(rows[0]) - 1
+    return [statistics.mean(row[j].elapsed_time(row[j + 1]) for row in rows) * 1e3 for j in range(n)]
+
+
+def per_launch_us(torch, graphs, reps, stream):
+    """Average duration of one launch, measured with an HIP event pair around
+    each replay of one-kernel graphs on the launch stream (so the idle time
+    between replays is not counted)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    with torch.cuda.stream(stream):
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record(stream)
+            graphs[i % len(graphs)].replay()
+            b.record(stream)
+        torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps * 1e3
+
+
+def bench_stream_chain(torch, tl, synth, dev, stream, dependent=True, reps=5):
+    """The 64-layer weight stream at M = 1 as one tl_linear_chain launch per
+    token: per layer q|k|v, o, gate|up, down (the linears that read one input
+    concatenated, one rotation each: 4 linears a layer), one layer generated
+    and replicated into 64 distinct sets of buffers.  With `dependent`,
+    every linear reads the binary16 output of the one before it (o the q part
+    of q|k|v, gate|up the output of o, down the gate part of gate|up, the next
+    layer's q|k|v the output of down), the data flow of a model whose
+    attention, norms and SwiGLU are left out; the scales are multiplied by
+    1/(0.02 sqrt(0.6 K)) so that the activations keep about unit variance
+    along the 256 dependent linears.  Otherwise each linear reads its own
+    synthetic input."""
+    import numpy as np
+
+    groups = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+    layer = []
+    for grp in groups:
+        k = synth.SHAPES[grp[0]][0]
+        ins = [synth.linear_inputs(synth.SHAPES[g][1], k, 1, seed=0, cfg=5, layer=0,
+                                   linear=synth.LINEAR_ID[g], outliers=g in ("q", "k", "v", "o"))
+               for g in grp]
+        sc = np.concatenate([i.scales for i in ins]).astype(np.float64)
+        if dependent:
+            sc = sc / (0.02 * np.sqrt(0.6 * k))
+        codes = torch.from_numpy(np.concatenate([i.codes for i in ins])).to(dev)
+        layer.append(dict(k=k, n=codes.shape[0], packed=tl.pack(codes, 1),
+                          scales=torch.from_numpy(sc.astype(np.float16)).to(dev),
+                          signs=torch.from_numpy(ins[0].signs).to(dev),
+                          x=torch.from_numpy(ins[0].x).to(dev).view(-1)))
+        del codes
+    ops, prev = [], None
+    weight_bytes = act_bytes = 0
+    for li in range(synth.N_LAYERS):
+        for spec in layer:
+            y = torch.empty(spec["n"], dtype=torch.float16, device=dev)
+            x = prev[:spec["k"]] if (dependent and prev is not None) else spec["x"]
+            p = spec["packed"] if li == 0 else spec["packed"].clone()
+            sc = spec["scales"] if li == 0 else spec["scales"].clone()
+            ops.append(dict(packed=p, scales=sc, fmt=1, x=x, signs=spec["signs"], y=y))
+            weight_bytes += p.numel() + sc.numel() * 2
+            act_bytes += 2 * spec["k"] + spec["k"] + 2 * spec["n"]
+            prev = y
+    chain = tl.Chain(ops)
+    with torch.cuda.stream(stream):
+        chain()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            chain()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    err = chain.error()
+    finite = bool(torch.isfinite(ops[-1]["y"].float()).all().item())
+    del g, chain, ops, layer, prev
+    torch.cuda.empty_cache()
+    if err != 0:
+        raise RuntimeError(f"tl_linear_chain reported error {err}")
+    return {"layers": synth.N_LAYERS, "linears_per_layer": len(groups),
+            "linears_per_launch": synth.N_LAYERS * len(groups), "launches_per_token": 1,
+            "dependent": dependent, "last_output_finite": finite,
+            "weight_bytes": int(weight_bytes), "activation_bytes": int(act_bytes),
+            "ms_per_token": round(ms, 4), "weight_streams_per_s": round(1e3 / ms, 1),
+            "GBs": round((weight_bytes + act_bytes) / (ms * 1e-3) / 1e9, 1)}
+
+
+def host_cpu() -> dict:
+    """The host's CPU: model name, logical CPUs, CPUs this process may use."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:   # pragma: no cover
+        usable = os.cpu_count() or 1
+    return {"model": model, "logical_cpus": os.cpu_count() or 1, "usable_cpus": usable}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -685,43 +949,101 @@ def main(argv=None) -> int:
         return profile_batched(torch, tl, synth, dev)
     if args.read_floor:
         return read_floor(torch, tl, dev)
-    log(f"building inputs fmt={args.fmt} copies={args.copies}")
+
+    extra = {}
+    if fmt == 1:
+        # the step: gate|up then down, two fused rotate + GEMV launches
+        log(f"building the step (gate|up, down), copies={args.copies}")
+        steps, launch_bytes = build_mlp_step(torch, tl, synth, dev, args.copies)
+        with torch.cuda.stream(stream):
+            step_graphs = capture(torch, lambda c: [fn() for fn in steps[c]], args.copies, stream)
+        log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+        ms = timed_replays(torch, step_graphs, args.steps, args.warmup, stream) / args.steps
+        sbytes = sum(launch_bytes)
+        launches = 2
+        per = per_launch_times_us(torch, steps, max(args.steps, 2 * args.copies), stream)
+        kern_us = sum(per) / len(per)
+        per_launch = sbytes / len(per)
+        kname = "gemv_m1_slot2_kernel<FL, true> (tl_linear, rotation fused): gate|up and down"
+        workload = ("decode step M=1 over the 27B-class MLP projections: gate|up (K=5120, "
+                    "N=2x17408, rows concatenated, one signed 1024-block Hadamard rotation of the "
+                    "input, binary16 output) then down (K=17408, N=5120) on the gate part of that "
+                    "output (the SwiGLU between them is outside the library), each one fused "
+                    "rotation + ternary g128 GEMV launch (tl_linear); binary16 activations, fp32 "
+                    "accumulation")
+        extra["step_launches"] = [
+            {"linear": "gate|up", "us": round(per[0], 3), "bytes": launch_bytes[0],
+             "GBs": round(launch_bytes[0] / (per[0] * 1e-6) / 1e9, 1)},
+            {"linear": "down", "us": round(per[1], 3), "bytes": launch_bytes[1],
+             "GBs": round(launch_bytes[1] / (per[1] * 1e-6) / 1e9, 1)}]
+        del step_graphs, steps
+        torch.cuda.empty_cache()
+        # the same step as one chain launch (down waits for gate|up on the device)
+        log("the step as one tl_linear_chain launch")
+        chains, cbytes = build_chain_step(torch, tl, synth, dev, args.copies)
+        with torch.cuda.stream(stream):
+            cg = capture(torch, lambda c: chains[c](), args.copies, stream)
+        cms = timed_replays(torch, cg, args.steps, args.warmup, stream) / args.steps
+        if any(c.error() for c in chains):
+            raise RuntimeError(f"tl_linear_chain reported errors {[c.error() for c in chains]}")
+        extra["step_as_chain"] = {"launches": 1, "ms_per_step": round(cms, 5),
+                                  "step_bytes": cbytes,
+                                  "step_GBs": round(cbytes / (cms * 1e-3) / 1e9, 1)}
+        del cg, chains
+        torch.cuda.empty_cache()
+    else:
+        ms = kern_us = per_launch = None
+    # the three projections as separate launches (tl_linear per projection)
+    log(f"separate launches per projection, fmt={args.fmt}")
     lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
     with torch.cuda.stream(stream):
-        step_graphs = capture(torch, lambda c: step_fn(tl, lins, fmt, c), args.copies, stream)
+        sep_graphs = capture(torch, lambda c: step_fn(tl, lins, fmt, c), args.copies, stream)
         gemv_graphs = capture(torch, lambda c: gemv_fn(tl, lins, fmt, c), args.copies, stream)
-    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    ms = timed_replays(torch, step_graphs, args.steps, args.warmup, stream) / args.steps
-    sbytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
-    value = sbytes / (ms * 1e-3) / 1e9
-
-    # the products alone on rotated activations (tl_gemv, 3 launches per replay)
+    sep_ms = timed_replays(torch, sep_graphs, args.steps, args.warmup, stream) / args.steps
+    sep_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) + rotate_bytes(1, l["k"]) for l in lins)
     reps = max(args.steps, 3 * args.copies)
     g_ms = timed_replays(torch, gemv_graphs, reps, args.warmup, stream)
     g_us = g_ms * 1e3 / (3 * reps)
     g_bytes = sum(gemv_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
-    # dominant kernel: the step is three launches of the fused rotate + GEMV
-    # kernel, so the step replays time it directly
-    avg_us = ms * 1e3 / 3.0
-    per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
-    kname = ("tl_linear (gemv_m1_slot2_kernel, rotation fused)" if fmt == 1 else
-             "tl_linear (gemv_trit5_kernel, rotation fused)")
-    achieved = per_launch / (avg_us * 1e-6) / 1e9
+    extra["separate_launches"] = {
+        "fmt": args.fmt, "launches": 3, "ms_per_step": round(sep_ms, 5), "step_bytes": sep_bytes,
+        "step_GBs": round(sep_bytes / (sep_ms * 1e-3) / 1e9, 1),
+        "gemv_alone_avg_launch_us": round(g_us, 3),
+        "gemv_alone_GBs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)}
+    if fmt != 1:
+        # dense trits: the three separate launches are the step
+        ms, sbytes, launches = sep_ms, sep_bytes, 3
+        sep_steps = [[(lambda l=l, c=c: tl.linear(l["packs"][c], l["scales"][c], fmt, l["x"],
+                                                  l["signs"], out=l["y"], x_rot=l["x_rot"]))
+                      for l in lins] for c in range(args.copies)]
+        per = per_launch_times_us(torch, sep_steps, reps, stream)
+        kern_us = sum(per) / len(per)
+        per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
+        kname = "gemv_trit5_kernel (tl_linear, rotation fused)"
+        workload = ("decode step M=1 over 27B-class MLP projections gate/up (K=5120, N=17408) and "
+                    "down (K=17408, N=5120): signed 1024-block Hadamard rotation + ternary g128 "
+                    "GEMV per projection (tl_linear, one launch each); binary16 activations, fp32 "
+                    "accumulation")
+    del sep_graphs, gemv_graphs, lins
+    torch.cuda.empty_cache()
+    value = sbytes / (ms * 1e-3) / 1e9
+    achieved = per_launch / (kern_us * 1e-6) / 1e9
     traffic = traffic_from_profiles(fmt)
+    rp = rocprof_launch_us(fmt)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None if traffic is None else round(traffic), "kernel": kname,
-                "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": round(per_launch)}
-    log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; dominant kernel avg {avg_us:.2f} us/launch, "
-        f"{achieved:.1f} GB/s; gemv alone {g_us:.2f} us/launch")
-    del step_graphs, gemv_graphs
+                "avg_launch_us": round(kern_us, 3),
+                "avg_launch_us_step_timed": round(ms * 1e3 / launches, 3),
+                "avg_launch_us_rocprof": rp,
+                "frac_rocprof": None if rp is None else round(per_launch / (rp * 1e-6) / 1e9 /
+                                                              HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": round(per_launch)}
+    log(f"step {ms * 1e3:.2f} us, {value:.1f} GB/s; dominant kernel {kern_us:.2f} us/launch, "
+        f"{achieved:.1f} GB/s; separate launches {sep_ms * 1e3:.2f} us/step")
 
-    extra = {"gemv_alone": {"avg_launch_us": round(g_us, 3),
-                            "GBs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)}}
     if not args.no_extra:
         other = 1 - fmt
-        del lins
-        torch.cuda.empty_cache()
         lins2 = build_step_inputs(torch, tl, synth, dev, other, args.copies)
         with torch.cuda.stream(stream):
             sg = capture(torch, lambda c: step_fn(tl, lins2, other, c), args.copies, stream)
@@ -729,7 +1051,7 @@ def main(argv=None) -> int:
         ms2 = timed_replays(torch, sg, args.steps, args.warmup, stream) / args.steps
         g2 = timed_replays(torch, gg, reps, args.warmup, stream)
         b2 = sum(gemv_bytes(l["n"], l["k"], 1, other) for l in lins2) / 3.0
-        extra["other_format"] = {
+        extra["other_format_separate_launches"] = {
             "fmt": "slot2" if other == 1 else "trit5",
             "step_GBs": round(sum(gemv_bytes(l["n"], l["k"], 1, other) + rotate_bytes(1, l["k"])
                                   for l in lins2) / (ms2 * 1e-3) / 1e9, 1),
@@ -738,6 +1060,16 @@ def main(argv=None) -> int:
             "gemv_GBs": round(b2 / (g2 * 1e-3 / (3 * reps)) / 1e9, 1)}
         del sg, gg, lins2
         torch.cuda.empty_cache()
+        log("64-layer weight stream as one chain launch per token (dependent linears)")
+        extra["weight_stream_chain"] = bench_stream_chain(torch, tl, synth, dev, stream, True)
+        log("64-layer weight stream as one chain launch per token (independent inputs)")
+        extra["weight_stream_chain_independent"] = bench_stream_chain(torch, tl, synth, dev, stream,
+                                                                      False)
+        log("64-layer weight stream, one tl_linear launch per linear")
+        extra["weight_stream"] = bench_stream(torch, tl, synth, dev, fmt, stream)
+        log("64-layer weight stream, one tl_linear launch per input (q|k|v and gate|up concatenated)")
+        extra["weight_stream_shared_rotation"] = bench_stream_shared(torch, tl, synth, dev, fmt,
+                                                                     stream)
         log("prefill GEMM (M = 512, 2048, 4096)")
         extra["gemm_prefill"] = bench_gemm(torch, tl, synth, dev, fmt)
         log("prefill GEMM with bfloat16 activations (M = 4096)")
@@ -747,11 +1079,6 @@ def main(argv=None) -> int:
         extra["batched_decode"] = bench_batched(torch, tl, synth, dev, fmt)
         log("rotation at prefill size")
         extra["rotate_prefill"] = bench_rotate_prefill(torch, tl, dev)
-        log("64-layer weight stream")
-        extra["weight_stream"] = bench_stream(torch, tl, synth, dev, fmt, stream)
-        log("64-layer weight stream, one rotation per input (q|k|v and gate|up concatenated)")
-        extra["weight_stream_shared_rotation"] = bench_stream_shared(torch, tl, synth, dev, fmt,
-                                                                     stream)
         log("weight quantiser (rotation folded in), gate and down")
         extra["quantize"] = bench_quantize(torch, tl, synth, dev)
         log("decode step with 1-bit weights")
@@ -769,13 +1096,9 @@ def main(argv=None) -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "decode step M=1 over 27B-class MLP projections gate/up "
-                               "(K=5120, N=17408) and down (K=17408, N=5120): signed "
-                               "1024-block Hadamard rotation + ternary g128 GEMV per "
-                               "projection (tl_linear); binary16 activations, fp32 "
-                               "accumulation",
-                   "format": args.fmt, "M": 1, "weight_copies": args.copies,
-                   "step_bytes": sbytes},
+        "config": {"workload": workload, "format": args.fmt, "M": 1,
+                   "weight_copies": args.copies, "step_bytes": sbytes,
+                   "launches_per_step": launches},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -52,9 +52,15 @@ using namespace m1;
 
 constexpr uint32_t kChainMagic = 0x4E484354u;
 constexpr int kChainFL = 6;       // weight steps per flight
-constexpr int kChainPre = 4;      // steps of the next linear requested before its input is ready
+constexpr int kChainCross = 4;    // steps of the next linear loaded during the current one
+constexpr int kChainMaxFlights = 3;   // flights of one linear (unrolled: no loop-carried loads)
 constexpr uint32_t kDefaultPolls = 1u << 20;
 constexpr int kFlagOffset = int(kLdsLimit) - 16;   // LDS word: this workgroup leaves the chain
+// per-segment partial sums of the current linear (at most kMaxSegsPerChunk
+// segments) at a fixed place, below the flag and above everything the next
+// linear's rotation and images use, so that wave 0 can add them up while the
+// other waves go on
+constexpr int kRedOffset = kFlagOffset - kMaxSegsPerChunk * 16;
 
 struct ChainHead {
     uint32_t magic;
@@ -79,7 +85,7 @@ static_assert(sizeof(ChainHead) == 64 && sizeof(ChainOp) == 64, "plan layout");
 // A linear as one workgroup sees it: its rows, its slot's segment range
 // (block-major, one chunk) and the buffer resources of its weight rows.
 struct OpState {
-    int nb, rows, beg, end, flights, row_bytes, groups;
+    int nb, rows, beg, end, steps, flights, row_bytes, groups;
     __amdgpu_buffer_rsrc_t wsrc, ssrc;
 };
 
@@ -87,7 +93,36 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int FL, int PRE>
+// Cache policy of the accesses that cross workgroups (a linear's output,
+// read as a later linear's input): coherent at device scope (sc1), so no
+// cache has to be written back or invalidated for them.
+constexpr int kDeviceScope = 16;
+
+// s_waitcnt immediate: vector memory count 0, the other counters not waited
+constexpr int kVmcntZero = 0x0F70;
+
+// rot::load with device-scope loads of x
+__device__ __forceinline__ void load_x_coherent(const uint16_t* x, const int8_t* signs, int nb,
+                                                int t, uint4 (&xr)[4], uint4 (&sr)[2]) {
+    const int hw = t >> 5, j = t & 31;
+    const __amdgpu_buffer_rsrc_t xs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, nb * 2048, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t ss =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, nb * 1024, kRsrcWord3);
+    const bool live = hw < nb;
+    const uint32_t xo = uint32_t((1024 * hw + 32 * j) * 2);
+    const uint32_t so = uint32_t(1024 * hw + 32 * j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              xs, live ? xo + 16 * i : kOob, 0, kDeviceScope));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        sr[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, live ? so + 16 * i : kOob, 0, 0));
+}
+
+template <int FL, int CROSS, int MAXF>
 __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restrict__ plan, int count,
                                                          uint32_t* sync) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -122,7 +157,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
         const int segs = st.rows * st.nb;
         st.beg = slot * segs / kSlots;
         st.end = (slot + 1) * segs / kSlots;
-        st.flights = ((segs + kSlots - 1) / kSlots + FL - 1) / FL;
+        st.steps = (segs + kSlots - 1) / kSlots;   // of the slot with the most
+        st.flights = (st.steps + FL - 1) / FL;
         st.wsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(op.packed + r0 * st.row_bytes),
                                                     0, st.rows * st.row_bytes, kRsrcWord3);
         st.ssrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(op.scales + r0 * st.groups),
@@ -130,73 +166,102 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
         return st;
     };
 
+    // The weight ring: wv[t], sv[t] hold step t of the flight being computed.
+    // As soon as step t is consumed, the same registers receive step t of the
+    // next flight, or, during a linear's last flight, step t < CROSS of the
+    // next linear's first flight (its steps CROSS.. are loaded after that
+    // linear's rotation, which needs their registers): FL steps per slot stay
+    // in flight within a linear, CROSS across its boundary.
     uint4 wv[FL];
     uint32_t sv[FL];
-    // weight and scale loads of steps [t_lo, t_hi) of flight f; steps past
-    // the slot's range read nothing (out-of-range offsets return zeros)
-    auto issue = [&](const OpState& st, int f, auto t_lo, auto t_hi) {
-        const int f0 = st.beg + f * FL;
-        const int rc = st.rows > 0 ? st.rows : 1;
-        int b = f0 / rc, r = f0 - (f0 / rc) * rc;
-#pragma unroll
-        for (int t = 0; t < FL; ++t) {
-            if (t >= decltype(t_lo)::value && t < decltype(t_hi)::value) {
-                const bool ok = f0 + t < st.end;
-                const uint32_t wo = ok ? uint32_t(r * st.row_bytes + 256 * b + 16 * u) : kOob;
-                const uint32_t so = ok ? uint32_t((r * st.groups + 8 * b + 2 * ip) * 2) : kOob;
-                wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(st.wsrc, wo, 0, 0));
-                sv[t] = __builtin_amdgcn_raw_buffer_load_b32(st.ssrc, so, 0, 0);
-            }
-            if (++r == rc) {
-                r = 0;
-                ++b;
-            }
+    // where the loads of a flight go: first segment, its block and row, and
+    // the linear's resources (selected among two linears with uniform selects)
+    struct Loads {
+        int f0, b, r, rc, end, row_bytes, groups;
+        __amdgpu_buffer_rsrc_t wsrc, ssrc;
+        bool live;
+    };
+    auto loads_of = [&](const OpState& s, int f, bool live) {
+        Loads l;
+        l.rc = s.rows > 0 ? s.rows : 1;
+        l.f0 = s.beg + f * FL;
+        l.b = l.f0 / l.rc;
+        l.r = l.f0 - l.b * l.rc;
+        l.end = s.end;
+        l.row_bytes = s.row_bytes;
+        l.groups = s.groups;
+        l.wsrc = s.wsrc;
+        l.ssrc = s.ssrc;
+        l.live = live;
+        return l;
+    };
+    // load step t of l into wv[t], sv[t] (steps past the slot's range, or of a
+    // dead flight, read nothing: out-of-range offsets return zeros); t is a
+    // constant after unrolling
+    auto load_step = [&](Loads& l, int t, bool want = true) {
+        const bool ok = want && l.live && l.f0 + t < l.end;
+        const uint32_t wo = ok ? uint32_t(l.r * l.row_bytes + 256 * l.b + 16 * u) : kOob;
+        const uint32_t so = ok ? uint32_t((l.r * l.groups + 8 * l.b + 2 * ip) * 2) : kOob;
+        wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(l.wsrc, wo, 0, 0));
+        sv[t] = __builtin_amdgcn_raw_buffer_load_b32(l.ssrc, so, 0, 0);
+        // keep the loads in step order: the compiler then waits for exactly
+        // the step it consumes (else it hoists the refills above the steps
+        // and waits for every load in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        if (++l.r == l.rc) {
+            l.r = 0;
+            ++l.b;
         }
     };
-    int cur_b = -1;
-    half8 a[8];
-    float rf = 0.0f, rx = 0.0f, ry = 0.0f;
-    auto run = [&](const OpState& st, int f, const uint8_t* img, const uint8_t* rec, float* red) {
-        const int f0 = st.beg + f * FL;
-        const int rc = st.rows > 0 ? st.rows : 1;
-        int b = f0 / rc, r = f0 - (f0 / rc) * rc;
+    auto load_steps = [&](Loads l, int t_lo, int t_hi) {
 #pragma unroll
-        for (int t = 0; t < FL; ++t) {
-            const bool ok = f0 + t < st.end;
-            if (ok && b != cur_b) {   // slot-uniform; rare (slots run block-major)
-                const uint8_t* src = img + b * kImgBlock + u * kImgLane;
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    a[j] = __builtin_bit_cast(
-                        half8, *reinterpret_cast<const lds_u32x4*>(lds_addr(src + 16 * j)));
-                const float4 rv = *reinterpret_cast<const float4*>(rec + (b * 4 + ip) * kRecBytes);
-                rf = rv.x;
-                rx = rv.y;
-                ry = rv.z;
-                cur_b = b;
+        for (int t = 0; t < FL; ++t)
+            if (t >= t_lo && t < t_hi)
+                load_step(l, t);
+            else if (++l.r == l.rc) {
+                l.r = 0;
+                ++l.b;
             }
-            const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
-            const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
-            float4v dx = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-            float4v dy = float4v{0.0f, 0.0f, 0.0f, 0.0f};
-            dx = mac_eword(p01[0], a[0], a[1], dx);
-            dy = mac_eword(p01[1], a[2], a[3], dy);
-            dx = mac_eword(p23[0], a[4], a[5], dx);
-            dy = mac_eword(p23[1], a[6], a[7], dy);
-            const float part = (h2f(sv[t] & 0xFFFFu) * (pick(dx, ip) + rx) +
-                                h2f(sv[t] >> 16) * (pick(dy, ip) + ry)) *
-                               rf;
-            if (diag && ok) red[(r * st.nb + b) * 4 + ip] = part;
-            if (++r == rc) {
-                r = 0;
-                ++b;
-            }
-        }
     };
-
-    using Zero = std::integral_constant<int, 0>;
-    using Pre = std::integral_constant<int, PRE>;
-    using All = std::integral_constant<int, FL>;
+    // step t of flight f of the current linear, then the refill of its
+    // registers; a[], rf, rx, ry: the activation images of block cur_b
+    auto step = [&](const OpState& st, int& b, int& r, int f0, Loads& nl, const uint8_t* img,
+                    const uint8_t* rec, float* red, int t, bool live, bool refill, int& cur_b,
+                    half8 (&a)[8], float& rf, float& rx, float& ry) {
+        const int rc = st.rows > 0 ? st.rows : 1;
+        const bool ok = f0 + t < st.end;
+        // steps past every slot's range (workgroup-uniform) only refill the ring
+        if (live) {
+        if (ok && b != cur_b) {   // slot-uniform; rare (slots run block-major)
+            const uint8_t* src = img + b * kImgBlock + u * kImgLane;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                a[j] = __builtin_bit_cast(half8,
+                                          *reinterpret_cast<const lds_u32x4*>(lds_addr(src + 16 * j)));
+            const float4 rv = *reinterpret_cast<const float4*>(rec + (b * 4 + ip) * kRecBytes);
+            rf = rv.x;
+            rx = rv.y;
+            ry = rv.z;
+            cur_b = b;
+        }
+        const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
+        const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
+        float4v dx = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        float4v dy = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+        dx = mac_eword(p01[0], a[0], a[1], dx);
+        dy = mac_eword(p01[1], a[2], a[3], dy);
+        dx = mac_eword(p23[0], a[4], a[5], dx);
+        dy = mac_eword(p23[1], a[6], a[7], dy);
+        const float part =
+            (h2f(sv[t] & 0xFFFFu) * (pick(dx, ip) + rx) + h2f(sv[t] >> 16) * (pick(dy, ip) + ry)) * rf;
+        if (diag && ok) red[(r * st.nb + b) * 4 + ip] = part;
+        if (++r == rc) {
+            r = 0;
+            ++b;
+        }
+        }
+        load_step(nl, t, refill);
+    };
 
     const bool plan_ok = head->magic == kChainMagic && head->count == count && head->grid == grid;
     if (!plan_ok) {
@@ -208,14 +273,21 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
     } else {
         const uint32_t max_polls = head->max_polls;
         OpState st = state(ops[0]);
-        issue(st, 0, Zero{}, Pre{});
+        load_steps(loads_of(st, 0, true), 0, CROSS);
         for (int i = 0; i < count; ++i) {
             const ChainOp op = ops[i];
             const int nb = st.nb;
             uint16_t* xrot = reinterpret_cast<uint16_t*>(smem);
             uint8_t* img = smem + nb * 2048;
             uint8_t* rec = img + nb * kImgBlock;
-            float* red = reinterpret_cast<float*>(rec + nb * 4 * kRecBytes);
+            float* red = reinterpret_cast<float*>(smem + kRedOffset);
+            // the next linear: its first CROSS steps are loaded during this
+            // linear's last flight, except by wave 0, which stores this
+            // linear's output and publishes it (a wait for its stores would
+            // also wait for such loads) and may poll for the next input: wave 0
+            // loads them once that is done
+            const bool has_next = i + 1 < count;
+            const OpState nx = has_next ? state(ops[i + 1]) : st;
 
             // the input: when an earlier linear of the chain writes it, wait
             // until every workgroup has written its rows
@@ -239,20 +311,17 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
                         }
                         *leave = bad;
                     }
-                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-                    if (i > 0) issue(st, 0, Zero{}, Pre{});
                 }
                 lds_barrier();
                 if (__builtin_amdgcn_readfirstlane(*leave)) break;
-            } else if (i > 0 && wave == 0) {
-                issue(st, 0, Zero{}, Pre{});
             }
+            if (i > 0 && wave == 0) load_steps(loads_of(st, 0, true), 0, CROSS);
 
             // rotation of the input into LDS (x_rot written by workgroup 0),
             // then the activation images
             {
                 uint4 xraw[4], sr[2];
-                rot::load(op.x, op.signs, nb, tid, xraw, sr);
+                load_x_coherent(op.x, op.signs, nb, tid, xraw, sr);
                 rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
                          kBlock);   // nb <= 32 half-waves
                 lds_barrier();
@@ -264,56 +333,78 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
                 lds_barrier();
             }
 
-            // the weight stream
-            cur_b = -1;
-            issue(st, 0, Pre{}, All{});
-            run(st, 0, img, rec, red);
-            for (int f = 1; f < st.flights; ++f) {
-                issue(st, f, Zero{}, All{});
-                run(st, f, img, rec, red);
-            }
-            lds_barrier();
-
-            // this workgroup's rows of y, in a fixed order: blocks ascending,
-            // the four columns of each block
-            const int64_t r0 = int64_t(bid) * (op.n / grid) + min(bid, op.n % grid);
-            for (int r = tid; r < st.rows; r += kThreads) {
-                const float4* pr = reinterpret_cast<const float4*>(red + r * nb * 4);
-                float v = 0.0f;
-                for (int b = 0; b < nb; ++b) {
-                    const float4 p = pr[b];
-                    v = (((v + p.x) + p.y) + p.z) + p.w;
+            // the weight stream: the first flight's steps not loaded during the
+            // previous linear (their registers stay free during the rotation)
+            // (nothing else may be in flight before them: a real wait
+            // instruction, which the compiler's wait placement accounts for)
+            __builtin_amdgcn_s_waitcnt(kVmcntZero);
+            load_steps(loads_of(st, 0, true), CROSS, FL);
+            int cur_b = -1;
+            half8 a[8];
+            float rf = 0.0f, rx = 0.0f, ry = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a[j] = half8{};
+            // (the flights are unrolled: a loop would carry loads in flight
+            // across its back edge, and the compiler then waits for all of
+            // them at the top of every flight)
+#pragma unroll
+            for (int f = 0; f < MAXF; ++f) {
+                if (f < st.flights) {
+                    const int f0 = st.beg + f * FL;
+                    const int rc = st.rows > 0 ? st.rows : 1;
+                    int b = f0 / rc, r = f0 - (f0 / rc) * rc;
+                    const bool last = f + 1 == st.flights;
+                    const int left = st.steps - f * FL;
+                    Loads nl = last ? loads_of(nx, 0, has_next && wave != 0) : loads_of(st, f + 1, true);
+#pragma unroll
+                    for (int t = 0; t < FL; ++t)
+                        step(st, b, r, f0, nl, img, rec, red, t, t < left, !last || t < CROSS, cur_b,
+                             a, rf, rx, ry);
                 }
-                if (op.y_f16)
-                    reinterpret_cast<__half*>(op.y)[r0 + r] = __float2half_rn(v);
-                else
-                    reinterpret_cast<float*>(op.y)[r0 + r] = v;
             }
-            // publish them: every thread's stores, then the counter
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            if (st.flights == 0 && has_next && wave != 0) load_steps(loads_of(nx, 0, true), 0, CROSS);
             lds_barrier();
-            if (tid == 0)
-                __hip_atomic_fetch_add(done + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-            // the next linear's first weight steps, before its input is ready
-            // (wave 0 after its wait)
-            if (i + 1 < count) {
-                st = state(ops[i + 1]);
-                if (wave != 0) issue(st, 0, Zero{}, Pre{});
+            // this workgroup's rows of y, added by wave 0 in a fixed order
+            // (blocks ascending, the four columns of each block), stored with
+            // device-scope stores, then published: once they are complete,
+            // the linear's counter goes up
+            if (wave == 0) {
+                const int64_t r0 = int64_t(bid) * (op.n / grid) + min(bid, op.n % grid);
+                const int esz = op.y_f16 ? 2 : 4;
+                const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(
+                    static_cast<uint8_t*>(op.y) + r0 * esz, 0, st.rows * esz, kRsrcWord3);
+                for (int r = lane; r < st.rows; r += 64) {
+                    const float4* pr = reinterpret_cast<const float4*>(red + r * nb * 4);
+                    float v = 0.0f;
+                    for (int b = 0; b < nb; ++b) {
+                        const float4 p = pr[b];
+                        v = (((v + p.x) + p.y) + p.z) + p.w;
+                    }
+                    if (op.y_f16)
+                        __builtin_amdgcn_raw_buffer_store_b16(uint16_t(f2h(v)), ys, uint32_t(2 * r),
+                                                              0, kDeviceScope);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ys,
+                                                              uint32_t(4 * r), 0, kDeviceScope);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+                if (lane == 0)
+                    __hip_atomic_fetch_add(done + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+            st = nx;
         }
     }
 
     // leave: loads of a linear the chain did not reach may still be in
     // flight; then the last workgroup out resets the counters for the next
     // call
+    // (this also completes the counter updates before the exit count)
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
     if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t before =
             __hip_atomic_fetch_add(exited, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (before == uint32_t(grid - 1)) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             for (int j = 0; j < count; ++j)
                 __hip_atomic_store(done + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(exited, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -321,8 +412,10 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
     }
 }
 
-int64_t lds_need(int64_t nb, int64_t rows) {
-    const int64_t tail = nb * kImgBlock + nb * 4 * kRecBytes + rows * nb * 16;
+// LDS below the partial sums: rotated input, then the images and records,
+// which first hold the rotation's transpose scratch
+int64_t lds_need(int64_t nb) {
+    const int64_t tail = nb * kImgBlock + nb * 4 * kRecBytes;
     const int64_t scratch = nb * rot::kScratchBytes;
     return nb * 2048 + (tail > scratch ? tail : scratch);
 }
@@ -367,7 +460,7 @@ int chain_encode(const tl_chain_op* ops, int32_t count, void* plan_out) {
             o.K / kBlock * 32 > kThreads)
             return TL_ERR_SHAPE;
         const int64_t nb = o.K / kBlock, rows = (o.N + grid - 1) / grid;
-        if (rows * nb > kMaxSegsPerChunk || lds_need(nb, rows) > kFlagOffset ||
+        if (rows * nb > int64_t(kSlots) * kChainFL * kChainMaxFlights || lds_need(nb) > kRedOffset ||
             rows * (o.K / 4) >= (int64_t(1) << 31))
             return TL_ERR_SHAPE;
         if (!aligned16(o.packed) || !aligned16(o.scales) || !aligned16(o.x) || !aligned16(o.signs) ||
@@ -421,10 +514,10 @@ int chain_encode(const tl_chain_op* ops, int32_t count, void* plan_out) {
 }
 
 hipError_t launch_chain(const void* plan, int32_t count, uint32_t* sync, hipStream_t stream) {
-    const hipError_t e = allow_lds(reinterpret_cast<const void*>(chain_kernel<kChainFL, kChainPre>),
+    const hipError_t e = allow_lds(reinterpret_cast<const void*>(chain_kernel<kChainFL, kChainCross, kChainMaxFlights>),
                                    int(kLdsLimit));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((chain_kernel<kChainFL, kChainPre>), dim3(unsigned(cu_count())), dim3(kThreads),
+    hipLaunchKernelGGL((chain_kernel<kChainFL, kChainCross, kChainMaxFlights>), dim3(unsigned(cu_count())), dim3(kThreads),
                        kLdsLimit, stream, static_cast<const uint8_t*>(plan), int(count), sync);
     return hipGetLastError();
 }
