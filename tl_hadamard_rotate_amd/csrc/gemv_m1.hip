@@ -55,6 +55,9 @@ namespace {
 
 using namespace m1;
 
+constexpr int kRingFlights = 3;   // flights of a chunk streamed as a ring: up to 4 in all
+constexpr int kRingMaxFL = 6;     // flight length of the ring (8 does not fit the registers)
+
 // ROT: x is the unrotated activations and signs their signs; the workgroup
 // rotates them in LDS first, and workgroup 0 also writes them to x_rot.
 template <int FL, bool ROT>
@@ -133,9 +136,16 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     int cur_b = -1;
     half8 a[8];
     float rf = 0.0f, rx = 0.0f, ry = 0.0f;
-    auto run = [&](int f) {
+    // Flight f.  With RING, as soon as step t is consumed its registers
+    // receive step t of flight f + 1 (the loads stay in step order, so the
+    // compiler waits for exactly the step it consumes): the weight stream
+    // does not pause between flights.
+    auto run = [&](int f, auto ring_c) {
+        constexpr bool RING = decltype(ring_c)::value;
         const int f0 = beg + f * FL;
         int b = f0 / rc, r = f0 - (f0 / rc) * rc;
+        const int g0 = f0 + FL;
+        int b2 = g0 / rc, r2 = g0 - (g0 / rc) * rc;
 #pragma unroll
         for (int t = 0; t < FL; ++t) {
             const bool ok = f0 + t < end;
@@ -167,8 +177,22 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
                 r = 0;
                 ++b;
             }
+            if constexpr (RING) {
+                const bool ok2 = g0 + t < end;
+                const uint32_t wo = ok2 ? uint32_t((rc0 + r2) * row_bytes + 256 * b2 + 16 * u) : kOob;
+                const uint32_t so = ok2 ? uint32_t(((rc0 + r2) * groups + 8 * b2 + 2 * ip) * 2) : kOob;
+                wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
+                sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (++r2 == rc) {
+                    r2 = 0;
+                    ++b2;
+                }
+            }
         }
     };
+    using Plain = std::false_type;
+    using Ring = std::true_type;
     auto finish_chunk = [&]() {
         lds_barrier();
         for (int r = tid; r < rc; r += kThreads) {
@@ -244,18 +268,32 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);   // nb * 32 <= kThreads
     }
     lds_barrier();
-    issue(0, Head{}, All{});
-    run(0);
-    for (int f = 1; f < flights; ++f) {
-        issue(f, Zero{}, All{});
-        run(f);
+    if (FL <= kRingMaxFL && flights > 1 && flights <= kRingFlights + 1) {
+        // the first chunk's flights as a ring (unrolled: a loop would carry
+        // loads in flight across its back edge, and the compiler would then
+        // wait for all of them at the top of every flight); nothing else is
+        // in flight when it starts (a real wait instruction, which the
+        // compiler's wait placement takes into account)
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vector memory count 0
+        issue(0, Head{}, All{});
+#pragma unroll
+        for (int f = 0; f < kRingFlights; ++f)
+            if (f + 1 < flights) run(f, Ring{});
+        run(flights - 1, Plain{});
+    } else {
+        issue(0, Head{}, All{});
+        run(0, Plain{});
+        for (int f = 1; f < flights; ++f) {
+            issue(f, Zero{}, All{});
+            run(f, Plain{});
+        }
     }
     finish_chunk();
     for (int c0 = rows_per_chunk; c0 < rows; c0 += rows_per_chunk) {
         set_chunk(c0);
         for (int f = 0; f < flights; ++f) {
             issue(f, Zero{}, All{});
-            run(f);
+            run(f, Plain{});
         }
         finish_chunk();
     }
@@ -303,6 +341,11 @@ hipError_t launch_m1(const uint8_t* packed, const uint16_t* scales, const uint16
                      const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k, void* y, int y_f16,
                      hipStream_t stream) {
     const M1Plan p = m1_plan(n, k, ROT);
+    // up to 8 steps a slot: one flight, every load issued at once; up to
+    // 4 flights of kRingMaxFL: a ring; beyond, flights of 8
+    if (p.steps > 8 && p.steps <= kRingMaxFL * (kRingFlights + 1))
+        return launch_fl<kRingMaxFL, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k,
+                                          p.rpc, y, y_f16, stream);
     switch (p.steps) {
         case 1:
             return launch_fl<1, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
