@@ -1,0 +1,103 @@
+"""GPU parity of the few-token decode GEMV with 2-bit slots (tl_gemv at
+2 <= M <= 16): tokens ride on the matrix-core rows, 8 rows of weights per
+unit, 8 tokens per pass (fewer when their activation images do not fit in
+LDS), one launch per pass.  Shapes cover a ragged last unit of rows, fewer
+rows than a unit, one 1024-block, partial passes (M not a multiple of the
+pass), two passes, passes of 2 at K = 17408, and a row count that needs
+several row chunks per workgroup.  Every output (or, at the largest N, a
+sample of rows in every tile) is compared with the oracle's product on the
+same binary16 activations (exact products, fp32 sums: relative L2 < 1e-5
+per token) and with the fp64 layer (2e-3)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import tl_hadamard_rotate_amd as tl
+
+pytestmark = pytest.mark.gpu
+
+SLOT2 = tl.FMT_SLOT2
+
+
+def dev(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def _per_token_err(y, want):
+    d = np.linalg.norm(y - want, axis=1)
+    w = np.linalg.norm(want, axis=1)
+    return float(np.max(d / np.maximum(w, 1e-300)))
+
+
+@pytest.mark.parametrize("m,n,k", [
+    (2, 1000, 2048), (3, 67, 1024), (5, 5, 1024), (7, 300, 3072), (8, 1000, 5120),
+    (9, 130, 1024), (13, 777, 6144), (16, 4097, 2048), (2, 1024, 17408), (3, 333, 17408),
+    (4, 515, 17408), (6, 2051, 4096)])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16], ids=["f32", "f16"])
+def test_gemv_few_tokens_every_output(gpu, m, n, k, out_dtype):
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=7 * m + n, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+    x_rot16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
+    y = host(tl.gemv(packed, dev(inp.scales, gpu), SLOT2, dev(x_rot16, gpu),
+                     out_dtype=out_dtype)).astype(np.float64)
+    want16 = oracle.matvec(inp.codes, inp.scales, x_rot16)
+    # binary16 outputs: the fp32 sum rounded once more (half an ulp, 2^-11)
+    assert _per_token_err(y, want16) < (1e-5 if out_dtype == torch.float32 else 1e-3)
+    assert oracle.rel_l2(y, oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)) < 2e-3
+
+
+def test_gemv_few_tokens_row_chunks(gpu):
+    """gate|up concatenated (N = 34816, K = 5120) at M = 8: a
+    workgroup's 136 rows take two row chunks of partial sums; sampled rows in
+    every 64-row tile, all tokens."""
+    k, n, m = 5120, 34816, 8
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=11, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+    x_rot16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
+    y = host(tl.gemv(packed, dev(inp.scales, gpu), SLOT2, dev(x_rot16, gpu))).astype(np.float64)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([np.arange(0, n, 64), np.arange(63, n, 64),
+                                     rng.integers(0, n, size=400)]))
+    want16 = oracle.matvec(inp.codes[rows], inp.scales[rows], x_rot16)
+    assert _per_token_err(y[:, rows], want16) < 1e-5
+
+
+def test_gemv_few_tokens_scale_per_token(gpu):
+    """Tokens of very different magnitudes (factors 2^-12 .. 2^4, one all
+    zero) in one launch: each token's activations are scaled on their own,
+    so every token keeps the fp32 bar."""
+    m, n, k = 8, 640, 4096
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=3, outliers=False)
+    x_rot = oracle.rotate(inp.x, inp.signs)
+    f = np.array([1.0, 2.0 ** -12, 2.0 ** 4, 0.0, 2.0 ** -6, 1.0, 2.0 ** 3, 2.0 ** -9])
+    x_rot16 = (x_rot * f[:, None]).astype(np.float16)
+    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+    y = host(tl.gemv(packed, dev(inp.scales, gpu), SLOT2, dev(x_rot16, gpu))).astype(np.float64)
+    want16 = oracle.matvec(inp.codes, inp.scales, x_rot16)
+    assert np.all(y[3] == 0.0)
+    live = [i for i in range(m) if i != 3]
+    assert _per_token_err(y[live], want16[live]) < 1e-5
+
+
+def test_gemv_few_tokens_deterministic_and_token_independent(gpu):
+    """Two calls give the same bits; a token's outputs do not depend on the
+    other tokens of its pass (token 0 alone at M = 2 with a zero partner
+    equals token 0 next to a random partner)."""
+    m, n, k = 8, 2048, 5120
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=5, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+    scales = dev(inp.scales, gpu)
+    x16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
+    a = host(tl.gemv(packed, scales, SLOT2, dev(x16, gpu)))
+    b = host(tl.gemv(packed, scales, SLOT2, dev(x16, gpu)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    pair = x16[:2].copy()
+    pair[1] = 0
+    c = host(tl.gemv(packed, scales, SLOT2, dev(pair, gpu)))
+    assert np.array_equal(c[0].view(np.uint32), a[0].view(np.uint32))

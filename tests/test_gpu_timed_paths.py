@@ -283,7 +283,7 @@ def bands_intact(buf):
 @pytest.mark.parametrize("fmt", FMTS + (tl.FMT_BIT1,), ids=["trit5", "slot2", "bit1"])
 @pytest.mark.parametrize("call,m,n,k", [
     ("gemv", 1, 67, 1024), ("gemv", 1, 4097, 2048), ("gemv", 3, 1000, 1024),
-    ("gemv", 17, 333, 1024), ("gemv", 1, 1, 17408), ("gemm", 65, 67, 1024),
+    ("gemv", 17, 333, 1024), ("gemv", 9, 333, 2048), ("gemv", 1, 1, 17408), ("gemm", 65, 67, 1024),
     ("gemm", 300, 1000, 2048), ("gemm", 257, 4099, 1024),
     ("linear", 1, 67, 1024), ("linear", 1, 5119, 6144), ("linear", 5, 300, 2048),
     ("linear", 70, 301, 1024)])

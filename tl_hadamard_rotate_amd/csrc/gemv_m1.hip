@@ -229,24 +229,17 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     // (built by the waves that hold activations), then the rest of the
     // weights.  Requested behind the whole weight stream, the activations
     // would arrive microseconds later (and requesting every step before the
-    // images was measured slower).  The activation loads are branch-free
-    // buffer loads, so no wave waits for them before its weight loads go out.
+    // images was measured slower).  Only the lanes that hold activations load
+    // them (loads that return zeros would still take the address units' time
+    // ahead of the weight loads), and no wave waits for them before its weight
+    // loads go out.
     uint4 xraw[4];
     if constexpr (ROT) {
         uint4 sr[2];
         rot::load(x, signs, nb, tid, xraw, sr);
         set_chunk(0);
         issue(0, Zero{}, Head{});
-        // the empty asm keeps the rotation below those weight loads
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            asm volatile("" : "+v"(xraw[i].x), "+v"(xraw[i].y), "+v"(xraw[i].z), "+v"(xraw[i].w)
-                         :
-                         : "memory");
-        asm volatile("" : "+v"(sr[0].x), "+v"(sr[0].y), "+v"(sr[0].z), "+v"(sr[0].w), "+v"(sr[1].x),
-                     "+v"(sr[1].y), "+v"(sr[1].z), "+v"(sr[1].w)
-                     :
-                     : "memory");
+        __builtin_amdgcn_sched_barrier(0);   // the rotation stays below those weight loads
         rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
                  kBlock);   // nb <= 32 half-waves
         lds_barrier();
@@ -259,12 +252,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         load_x(x, nb, tid, xraw);
         set_chunk(0);
         issue(0, Zero{}, Head{});
-        // the empty asm keeps the image build below those weight loads
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            asm volatile("" : "+v"(xraw[i].x), "+v"(xraw[i].y), "+v"(xraw[i].z), "+v"(xraw[i].w)
-                         :
-                         : "memory");
+        __builtin_amdgcn_sched_barrier(0);   // the image build stays below those weight loads
         if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);   // nb * 32 <= kThreads
     }
     lds_barrier();

@@ -88,13 +88,35 @@ __device__ __forceinline__ void load_x(const uint16_t* x, int nb, int t, uint4 (
     const int ep = img_ep(t);
     const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(x), 0, nb * 2048, kRsrcWord3);
-    const bool live = t < nb * 32;
+    // lanes past the last block issue nothing (loads that return zeros still
+    // take the address units' time ahead of the weight loads); their raw is
+    // left unset and never used
+    if (t < nb * 32) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t o = live ? uint32_t((1024 * b + eword_k(u, ep + 2 * h)) * 2) : kOob;
-        raw[2 * h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
-        raw[2 * h + 1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, live ? o + 16 : kOob, 0, 0));
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t o = uint32_t((1024 * b + eword_k(u, ep + 2 * h)) * 2);
+            raw[2 * h] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, o, 0, 0));
+            raw[2 * h + 1] =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, o + 16, 0, 0));
+        }
     }
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// s + (low or high binary16 half of w), in fp32 with one rounding (the half
+// converts exactly): one mixed-precision fma instead of a conversion and an add
+__device__ __forceinline__ float add_lo_half(float s, uint32_t w) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(s) : "v"(w));
+    return s;
+}
+__device__ __forceinline__ float add_hi_half(float s, uint32_t w) {
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(s) : "v"(w));
+    return s;
+}
+__device__ __forceinline__ _Float16 pow2h(int e) {   // 2^e for -14 <= e <= 15
+    return __builtin_bit_cast(_Float16, uint16_t((15 + e) << 10));
 }
 
 __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t* img, uint8_t* rec) {
@@ -103,14 +125,16 @@ __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t*
     const int u = img_u(t);
     const int ep = img_ep(t);
     // largest |x| of the column (bit patterns of non-negative binary16 values
-    // order like the values)
-    uint32_t m = 0;
+    // order like the values): packed 16-bit maxima of the magnitudes
+    u16x2 mv = {0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+        for (int j = 0; j < 4; ++j)
+            mv = __builtin_elementwise_max(mv, __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu));
     }
+    uint32_t m = max(uint32_t(mv.x), uint32_t(mv.y));
     m = max(m, dpp<kDppXor1>(m));
     m = max(m, dpp<kDppXor2>(m));
     m = max(m, dpp<kDppHalfMirror>(m));
@@ -119,30 +143,35 @@ __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t*
         ex = int(m >> 10) - 15;
     else if (m != 0u)
         ex = (31 - __builtin_clz(m)) - 24;
-    // pre-scale of in-word position j (its digit decodes to d * 2^(s_j - 24))
-    constexpr int kShift[8] = {4, 6, 4, 6, 8, 4, 6, 8};
-    float fc[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) fc[j] = pow2f(14 - kShift[j] - ex);
+    // At least -5, so that the three pre-scales below are binary16 numbers.
+    // Nothing is lost: a column whose largest |x| is below 2^-5 is scaled by
+    // 2^15 (instead of more) and every binary16 x times 2^11..2^15 is still
+    // an exact normal binary16 number; the sums scale by a power of two.
+    ex = max(ex, -5);
+    // pre-scale of in-word position j (its digit decodes to d * 2^(s_j - 24)),
+    // s_j = 4, 6, 4, 6, 8, 4, 6, 8: factor 2^(14 - s_j - ex)
+    const _Float16 f4 = pow2h(10 - ex), f6 = pow2h(8 - ex), f8 = pow2h(6 - ex);
+    const _Float16 fc[8] = {f4, f6, f4, f6, f8, f4, f6, f8};
     u32x4* dst = reinterpret_cast<u32x4*>(img + b * kImgBlock + u * kImgLane);
     float sum = 0.0f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+        // x[16 h' + i] (i = 0..15 of this e-word pair) at half i of w
         const uint32_t w[8] = {raw[2 * h].x, raw[2 * h].y, raw[2 * h].z, raw[2 * h].w,
                                raw[2 * h + 1].x, raw[2 * h + 1].y, raw[2 * h + 1].z,
                                raw[2 * h + 1].w};
-        float v[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v[2 * j] = h2f(w[j] & 0xFFFFu);
-            v[2 * j + 1] = h2f(w[j] >> 16);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) sum += v[j];
-        // pair j faces digits (j, 8 + j)
+        for (int j = 0; j < 8; ++j) sum = add_hi_half(add_lo_half(sum, w[j]), w[j]);
+        // pair j faces digits (j, 8 + j): halves j and 8 + j side by side,
+        // times the pair's factor (binary16 product, rounded once as the
+        // fp32 product rounded to binary16 would be)
         uint32_t out[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out[j] = f2h(v[j] * fc[j]) | (f2h(v[8 + j] * fc[j]) << 16);
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t pr = __builtin_amdgcn_perm(w[4 + j / 2], w[j / 2],
+                                                      (j & 1) ? 0x07060302u : 0x05040100u);
+            out[j] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2v, pr) * half2v{fc[j], fc[j]});
+        }
         const int e = ep + 2 * h;
         if (live) {
             dst[2 * e] = u32x4{out[0], out[1], out[2], out[3]};

@@ -34,9 +34,9 @@ __device__ __forceinline__ uint32_t f2h(float f) {
 }
 
 // The loads of thread t: x[1024 hw + 32 j ...] (64 bytes) and its signs (32
-// bytes).  Buffer loads with no branch: lanes past the last block get an
-// offset beyond the buffer and read zeros, so no lane waits for them before
-// issuing what follows.
+// bytes).  Lanes past the last block issue nothing (loads that return zeros
+// still take the address units' time ahead of what follows) and leave xr and
+// sr unset; run() does nothing for them.
 __device__ __forceinline__ void load(const uint16_t* x, const int8_t* signs, int nb, int t,
                                      uint4 (&xr)[4], uint4 (&sr)[2]) {
     const int hw = t >> 5, j = t & 31;
@@ -44,17 +44,15 @@ __device__ __forceinline__ void load(const uint16_t* x, const int8_t* signs, int
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, nb * 2048, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t ss =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, nb * 1024, kRsrcWord3);
-    const bool live = hw < nb;
+    if (hw >= nb) return;
     const uint32_t xo = uint32_t((1024 * hw + 32 * j) * 2);
     const uint32_t so = uint32_t(1024 * hw + 32 * j);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        xr[i] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, live ? xo + 16 * i : kOob, 0, 0));
+        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, xo + 16 * i, 0, 0));
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        sr[i] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, live ? so + 16 * i : kOob, 0, 0));
+        sr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, so + 16 * i, 0, 0));
 }
 
 template <int H>
