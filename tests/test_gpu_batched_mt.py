@@ -87,8 +87,8 @@ def test_gemv_few_tokens_scale_per_token(gpu):
 
 def test_gemv_few_tokens_deterministic_and_token_independent(gpu):
     """Two calls give the same bits; a token's outputs do not depend on the
-    other tokens of its pass (token 0 alone at M = 2 with a zero partner
-    equals token 0 next to a random partner)."""
+    other tokens of its pass (token 0 next to zero partners equals token 0
+    next to random ones, at M = 8 and at M = 2)."""
     m, n, k = 8, 2048, 5120
     inp = synth.linear_inputs(n, k, m, cfg=3, linear=5, outliers=True)
     packed = tl.pack(dev(inp.codes, gpu), SLOT2)
@@ -97,7 +97,9 @@ def test_gemv_few_tokens_deterministic_and_token_independent(gpu):
     a = host(tl.gemv(packed, scales, SLOT2, dev(x16, gpu)))
     b = host(tl.gemv(packed, scales, SLOT2, dev(x16, gpu)))
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    pair = x16[:2].copy()
-    pair[1] = 0
-    c = host(tl.gemv(packed, scales, SLOT2, dev(pair, gpu)))
-    assert np.array_equal(c[0].view(np.uint32), a[0].view(np.uint32))
+    for mm in (8, 2):
+        rand = host(tl.gemv(packed, scales, SLOT2, dev(x16[:mm], gpu)))
+        lone = x16[:mm].copy()
+        lone[1:] = 0
+        c = host(tl.gemv(packed, scales, SLOT2, dev(lone, gpu)))
+        assert np.array_equal(c[0].view(np.uint32), rand[0].view(np.uint32)), mm

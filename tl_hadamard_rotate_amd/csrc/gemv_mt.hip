@@ -21,7 +21,10 @@
 // see one group, exactly as at M = 1.  The byte offset of a lane in the chunk
 // (16 * (4 * c' + q), c' = chunk within its 1024-block) is the M = 1 kernel's
 // lane rank u = 4 * c' + q, so a token's activation image is the M = 1 image
-// and one token's image serves every row of the workgroup.
+// and one token's image serves every row of the workgroup.  The two slots of a
+// wave take the two chunks of a chunk pair of the same 8 rows, so every load
+// instruction reads whole 128-byte lines (64-byte halves read at different
+// times were measured 0.2-0.3 us slower per launch).
 //
 // D rows 8s + 4h .. 8s + 4h + 3 (tokens 4h .. 4h + 3) land in the lanes with
 // q = 2s + h.  Those lanes scale the two groups' sums (binary16 scales, the
@@ -34,11 +37,12 @@
 // (from the L2 cache in practice: a workgroup's slice is tens of KB).
 //
 // Work split and memory pipeline as at M = 1: one 1024-thread workgroup per CU
-// owns a contiguous slice of rows; a slot takes a contiguous run of units in
-// chunk-major order (its activations change only when the chunk does); the
-// activations are requested first, then the first two steps' weights, then
-// the images are built, then the rest of the weights follow, all before the
-// slot's first wait on weights (a ring of flights past 8 steps).
+// owns a contiguous slice of rows; a wave takes a contiguous run of pair units
+// in pair-major order (its activations change only when the chunk pair does);
+// the activations are requested first (only by lanes that hold some), then the
+// first two steps' weights, then the images are built, then the rest of the
+// weights follow, all before the wave's first wait on weights (a ring of
+// flights past 7 steps).
 #include <hip/hip_fp16.h>
 
 #include <type_traits>
@@ -52,7 +56,7 @@ namespace {
 using namespace m1;
 
 constexpr int kUnitRows = 8;                 // rows of a unit (columns of a slot)
-constexpr int kSlotsMt = 2 * kWaves;         // 32-lane slots per workgroup
+constexpr uint32_t kOnes = 0x55555555u;      // 16 digits 1 (codes 0)
 constexpr int kTokPad = 16;                  // bytes between token images (LDS bank spread)
 constexpr int kRingFlightsMt = 3;            // ring as in the M = 1 kernel: up to 4 flights
 constexpr int kRingMaxFLMt = 5;            // 6 does not fit the registers here
@@ -69,6 +73,11 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int mt, int64_t n,
     int64_t k, int row_base, int row_rem, int rows_per_chunk, void* __restrict__ y, int y_f16) {
     constexpr int V = MT < 4 ? MT : 4;       // tokens per D lane
+    // Where the groups' sums of x come from: at 8 tokens from the matrix cores
+    // once per chunk (the image build, which runs on every wave, is then the
+    // longer part of the prologue); with fewer, from the image build (the
+    // extra products slowed the stream more than the sums cost).
+    constexpr bool kMfmaOffsets = MT == 8;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int nb = int(k / kBlock);
     const int nch = 4 * nb;                  // 256-weight chunks of a row
@@ -82,9 +91,8 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15;
     const int q = lane >> 4;
-    const int s = col >> 3;                  // slot within the wave
+    const int s = col >> 3;                  // slot within the wave: chunk 2p + s of a pair
     const int ip = col & 7;                  // row of the unit; token of the A row
-    const int slot = 2 * wave + s;
     const int h = q - 2 * s;                 // lanes holding tokens 4h .. 4h + 3 of D
     const bool dlane = (q >> 1) == s && 4 * h < MT;
 
@@ -98,23 +106,27 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(scales + r0 * groups), 0, int(rows * groups * 2), kRsrcWord3);
 
-    // Per chunk of rows: G units of 8 rows per 256-weight chunk, the slot's unit
-    // range [beg, end) in chunk-major order (unit = c * G + g), in flights of FL.
+    // Per chunk of rows: G groups of 8 rows.  A wave's step is a pair unit:
+    // one group of 8 rows at the chunk pair (2p, 2p + 1), slot s taking chunk
+    // 2p + s, so the wave reads 128 contiguous bytes (whole cache lines) of
+    // each of its 8 rows.  The wave's pair units [beg, end) run pair-major
+    // (pair unit = p * G + g), in flights of FL.
     int rc0 = 0, rc = 0, G = 1, beg = 0, end = 0, flights = 0;
     auto set_chunk = [&](int c0) {
         rc0 = c0;
         rc = min(rows_per_chunk, rows - c0);
         G = (rc + kUnitRows - 1) / kUnitRows;
-        const int units = nch * G;
-        beg = slot * units / kSlotsMt;
-        end = (slot + 1) * units / kSlotsMt;
-        flights = ((units + kSlotsMt - 1) / kSlotsMt + FL - 1) / FL;   // workgroup-uniform
+        const int units = (nch / 2) * G;
+        beg = wave * units / kWaves;
+        end = (wave + 1) * units / kWaves;
+        flights = ((units + kWaves - 1) / kWaves + FL - 1) / FL;   // workgroup-uniform
     };
     uint4 wv[FL];
     uint32_t sv[FL];
     // offsets of step `u` (a unit index) for this lane; out-of-range -> kOob
-    auto offsets = [&](int u, int c, int g, uint32_t& wo, uint32_t& so) {
+    auto offsets = [&](int u, int pp, int g, uint32_t& wo, uint32_t& so) {
         const int r = kUnitRows * g + ip;
+        const int c = 2 * pp + s;
         const bool ok = u < end && r < rc;
         wo = ok ? uint32_t((rc0 + r) * row_bytes + 64 * c + 16 * q) : kOob;
         so = ok ? uint32_t(((rc0 + r) * groups + 2 * c) * 2) : kOob;
@@ -158,8 +170,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
 #pragma unroll
         for (int t = 0; t < FL; ++t) {
             const bool ok = f0 + t < end;
-            if (ok && c != cur_c) {   // slot-uniform; once per chunk (units run chunk-major)
-                const int b = c >> 2, cp = c & 3;
+            if (ok && c != cur_c) {   // wave-uniform; once per chunk pair (units run pair-major)
+                const int cl = 2 * c + s;   // this slot's chunk
+                const int b = cl >> 2, cp = cl & 3;
                 if (ip < mt) {
                     const uint8_t* src = img + ip * tstride + b * kImgBlock + (4 * cp + q) * kImgLane;
 #pragma unroll
@@ -173,8 +186,24 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
                         const float4 rv = *reinterpret_cast<const float4*>(
                             rec + (4 * h + v) * rec_tok_bytes(nb) + (4 * b + cp) * kRecBytes);
                         rf[v] = rv.x;
-                        ox[v] = rv.y;
-                        oy[v] = rv.z;
+                        if constexpr (!kMfmaOffsets) {
+                            ox[v] = -rv.y;
+                            oy[v] = -rv.z;
+                        }
+                    }
+                }
+                if constexpr (kMfmaOffsets) {
+                    // the digit offsets (sum of the group's x, image units) from
+                    // the matrix cores: the same products as a step whose digits
+                    // are all 1 (code 0), so all-zero codes cancel exactly
+                    const float4v sx =
+                        mac_eword(kOnes, a[4], a[5], mac_eword(kOnes, a[0], a[1], float4v{}));
+                    const float4v sy =
+                        mac_eword(kOnes, a[6], a[7], mac_eword(kOnes, a[2], a[3], float4v{}));
+#pragma unroll
+                    for (int v = 0; v < V; ++v) {
+                        ox[v] = sx[v];
+                        oy[v] = sy[v];
                     }
                 }
                 cur_c = c;
@@ -189,10 +218,10 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
             const float sa = h2f(sv[t] & 0xFFFFu), sb = h2f(sv[t] >> 16);
             float part[V];
 #pragma unroll
-            for (int v = 0; v < V; ++v) part[v] = (sa * (dx[v] + ox[v]) + sb * (dy[v] + oy[v])) * rf[v];
+            for (int v = 0; v < V; ++v) part[v] = (sa * (dx[v] - ox[v]) + sb * (dy[v] - oy[v])) * rf[v];
             const int r = kUnitRows * g + ip;
             if (dlane && ok && r < rc) {
-                float* dst = red + (r * MT + 4 * h) * nch + c;
+                float* dst = red + (r * MT + 4 * h) * nch + 2 * c + s;
 #pragma unroll
                 for (int v = 0; v < V; ++v) dst[v * nch] = part[v];
             }
@@ -276,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
         if (rd * kThreads + wave * 64 < tasks) {
             const int tk = tau / tasks_per_tok;
             const bool live = tau < tasks;
-            build_pass(xraw[rd], nb, live ? tau - tk * tasks_per_tok : tasks_per_tok,
+            build_pass<!kMfmaOffsets>(xraw[rd], nb, live ? tau - tk * tasks_per_tok : tasks_per_tok,
                        img + (live ? tk : 0) * tstride, rec + (live ? tk : 0) * rec_tok_bytes(nb));
         }
     }
@@ -312,7 +341,7 @@ struct MtPlan {
     unsigned grid;
     int mt;        // tokens per pass
     int rpc;       // rows per chunk
-    int steps;     // steps per slot and chunk
+    int steps;     // steps per wave and row chunk
     size_t lds;
 };
 
@@ -348,7 +377,7 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
     p.grid = unsigned(grid);
     p.rpc = int(rpc);
     const int64_t g = (rpc + kUnitRows - 1) / kUnitRows;
-    p.steps = int((4 * nb * g + kSlotsMt - 1) / kSlotsMt);
+    p.steps = int((2 * nb * g + kWaves - 1) / kWaves);
     p.lds = fixed + size_t(rpc) * size_t(4 * nb) * p.mt * 4;
     return p;
 }

@@ -119,6 +119,9 @@ __device__ __forceinline__ _Float16 pow2h(int e) {   // 2^e for -14 <= e <= 15
     return __builtin_bit_cast(_Float16, uint16_t((15 + e) << 10));
 }
 
+// SUMS: also the record's group sums (a kernel that takes them from the
+// matrix cores passes false; its records hold {2^(10+E), 0, 0, 0}).
+template <bool SUMS = true>
 __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t* img, uint8_t* rec) {
     const bool live = t < nb * 32;
     const int b = live ? t >> 5 : 0;
@@ -160,8 +163,10 @@ __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t*
         const uint32_t w[8] = {raw[2 * h].x, raw[2 * h].y, raw[2 * h].z, raw[2 * h].w,
                                raw[2 * h + 1].x, raw[2 * h + 1].y, raw[2 * h + 1].z,
                                raw[2 * h + 1].w};
+        if constexpr (SUMS) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) sum = add_hi_half(add_lo_half(sum, w[j]), w[j]);
+            for (int j = 0; j < 8; ++j) sum = add_hi_half(add_lo_half(sum, w[j]), w[j]);
+        }
         // pair j faces digits (j, 8 + j): halves j and 8 + j side by side,
         // times the pair's factor (binary16 product, rounded once as the
         // fp32 product rounded to binary16 would be)
@@ -180,9 +185,12 @@ __device__ inline void build_pass(const uint4 (&raw)[4], int nb, int t, uint8_t*
     }
     // the column's group sums: over the lane quad, then the other group's
     // from the other quad
-    sum += dppf<kDppXor1>(sum);
-    sum += dppf<kDppXor2>(sum);
-    const float other = dppf<kDppHalfMirror>(sum);
+    float other = 0.0f;
+    if constexpr (SUMS) {
+        sum += dppf<kDppXor1>(sum);
+        sum += dppf<kDppXor2>(sum);
+        other = dppf<kDppHalfMirror>(sum);
+    }
     if (live && (t & 7) == 0) {
         const float unit = pow2f(-10 - ex);
         *reinterpret_cast<float4*>(rec + (b * 4 + (u >> 2)) * kRecBytes) =
