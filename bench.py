@@ -262,7 +262,8 @@ def _event_time(torch, fn, reps):
 def bench_gemm(torch, tl, synth, dev, fmt, reps=5, bf16=False, ms_list=None):
     """Prefill GEMM TFLOP/s for M in {512, 2048, 4096} at the MLP shapes
     (gate: K=5120 N=17408, down: K=17408 N=5120); with bf16, tl_gemm_bf16 on
-    bfloat16 activations (bfloat16 matrix peak = the fp16 one)."""
+    bfloat16 activations (their conversion to binary16 included; bfloat16
+    matrix peak = the fp16 one)."""
     out = []
     call = tl.gemm_bf16 if bf16 else tl.gemm
     xdt = torch.bfloat16 if bf16 else torch.float16
@@ -275,8 +276,8 @@ def bench_gemm(torch, tl, synth, dev, fmt, reps=5, bf16=False, ms_list=None):
             gen = torch.Generator(device="cpu").manual_seed(4 + m)
             x = torch.randn((m, k), generator=gen).to(xdt).to(dev)
             y = torch.empty((m, n), dtype=torch.float32, device=dev)
-            ws = torch.empty(max(1, tl.gemm_workspace_bytes(m, n, k, fmt)), dtype=torch.uint8,
-                             device=dev)
+            size = tl.gemm_bf16_workspace_bytes if bf16 else tl.gemm_workspace_bytes
+            ws = torch.empty(max(1, size(m, n, k, fmt)), dtype=torch.uint8, device=dev)
             call(packed, scales, fmt, x, out=y, workspace=ws)
             torch.cuda.synchronize()
             ms = _event_time(torch, lambda i: call(packed, scales, fmt, x, out=y, workspace=ws),

@@ -132,15 +132,19 @@ TL_API tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t 
                   const uint16_t* x_rot, int64_t M, int64_t N, int64_t K,
                   void* y, int32_t y_dtype, hipStream_t stream);
 
-/* Bytes of device workspace that tl_gemm, tl_gemm_bf16 and tl_linear need
- * for this shape and format (0: none; tl_gemm_bf16 and tl_linear at M < 64
- * need at most this much).  Host only; it depends on the compute-unit count of
- * the current device.  Returns -1 when the shape or format is not accepted
- * (tl_gemm's rules).  The workspace holds, for dense trits and 1-bit codes,
- * the weights rewritten as 2-bit slots (N * K/4 bytes, rounded up to 256),
- * then, when output tiles are split along K, their fp32 partial sums (at most
- * 64 MiB). */
+/* Bytes of device workspace that tl_gemm and tl_linear need for this shape
+ * and format (0: none; tl_linear at M < 64 needs none).  Host only; it
+ * depends on the compute-unit count of the current device.  Returns -1 when
+ * the shape or format is not accepted (tl_gemm's rules).  The workspace
+ * holds, for dense trits and 1-bit codes, the weights rewritten as 2-bit
+ * slots (N * K/4 bytes, rounded up to 256), then, when output tiles are split
+ * along K, their fp32 partial sums (at most 64 MiB). */
 TL_API int64_t tl_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
+
+/* The same for tl_gemm_bf16: the rewrite as above, then the binary16 copy of
+ * the activations (M * K * 2 bytes) and M fp32 row factors (each rounded up
+ * to 256 bytes), then the K-split partial sums. */
+TL_API int64_t tl_gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt);
 
 /* Launch plan of tl_gemm for this shape (host only, for tests and tuning):
  * out[0] = output tiles of 256 x 256, out[1] = tiles computed whole, out[2] =
@@ -267,13 +271,14 @@ TL_API tl_status tl_linear_chain(const void* plan, int32_t count, uint32_t* sync
 
 /* The prefill product with bfloat16 rotated activations:
  *   y[m, n] = sum_g S[n, g] * sum_{k in g} code[n, k] * x_rot[m, k]
- * with the codes entering the matrix cores as exact bfloat16 -1/0/+1 and each
- * group's fp32 sum multiplied by its binary16 scale in fp32 (the scale is not
- * rounded to bfloat16).  x_rot: bfloat16 [M, K] passed as uint16 bits; every
- * other argument, rule and error as tl_gemm (the workspace holds only the
- * rewrite of dense trits and 1-bit codes as 2-bit slots; no K split).  For
- * models whose activations are bfloat16; the binary16 tl_gemm is the more
- * accurate product (bfloat16 keeps 8 significant bits against 11). */
+ * for models whose activations are bfloat16.  Each row of x_rot is scaled by
+ * the power of two that brings its largest |x| into [2^14, 2^15) and
+ * converted to binary16, which is exact for a bfloat16 number (8 significant
+ * bits) unless it is below 2^-17 of that range; the product then runs as
+ * tl_gemm's (exact binary16 code * scale, fp32 sums) and the outputs are
+ * multiplied back by the power of two.  x_rot: bfloat16 [M, K] passed as
+ * uint16 bits; workspace: at least tl_gemm_bf16_workspace_bytes; every other
+ * argument, rule and error as tl_gemm. */
 TL_API tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fmt,
                               const uint16_t* x_rot, int64_t M, int64_t N, int64_t K, void* y,
                               int32_t y_dtype, void* workspace, int64_t workspace_bytes,

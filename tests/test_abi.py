@@ -25,7 +25,7 @@ def _declared():
 def test_header_declares_the_four_calls():
     names = _declared()
     for need in ("tl_pack", "tl_hadamard_rotate", "tl_gemv", "tl_gemm", "tl_linear", "tl_quantize",
-                 "tl_gemm_workspace_bytes", "tl_gemm_plan"):
+                 "tl_gemm_workspace_bytes", "tl_gemm_bf16_workspace_bytes", "tl_gemm_plan"):
         assert need in names
 
 
@@ -134,8 +134,15 @@ def test_gemm_workspace_and_plan():
         rewrite = -(-(n * k // 4) // 256) * 256
         assert L.tl_gemm_workspace_bytes(m, n, k, 0) == rewrite + partial
         assert L.tl_gemm_workspace_bytes(m, n, k, 2) == rewrite + partial
+        # bfloat16 activations: their binary16 copy and the row factors
+        # between the rewrite and the partial sums
+        copy = -(-(m * k * 2) // 256) * 256 + -(-(m * 4) // 256) * 256
+        assert L.tl_gemm_bf16_workspace_bytes(m, n, k, 1) == copy + partial
+        assert L.tl_gemm_bf16_workspace_bytes(m, n, k, 0) == rewrite + copy + partial
     assert L.tl_gemm_workspace_bytes(64, 1024, 1000, 1) == -1
     assert L.tl_gemm_workspace_bytes(64, 1024, 1024, 9) == -1
+    assert L.tl_gemm_bf16_workspace_bytes(64, 1024, 1000, 1) == -1
+    assert L.tl_gemm_bf16_workspace_bytes(64, 1024, 1024, 9) == -1
     assert L.tl_gemm_plan(64, 1024, 1024, NULL) == 1
     out = (ctypes.c_int64 * 3)()
     assert L.tl_gemm_plan(0, 1024, 1024, out) == 2
@@ -145,10 +152,12 @@ def test_gemm_workspace_and_plan():
 @pytest.mark.parametrize("call", ["tl_gemm", "tl_gemm_bf16"])
 def test_gemm_workspace_validation(call):
     fn = getattr(tl.lib(), call)
-    need = tl.lib().tl_gemm_workspace_bytes(64, 1024, 1024, 0)
-    rewrite = 1024 * 1024 // 4        # all tl_gemm_bf16 needs: no K split
+    size = tl.lib().tl_gemm_bf16_workspace_bytes if call == "tl_gemm_bf16" else \
+        tl.lib().tl_gemm_workspace_bytes
+    need = size(64, 1024, 1024, 0)
+    assert need >= 1024 * 1024 // 4
     assert _gemv(fn, m=64, n=1024, ws=NULL, ws_bytes=0) == 8            # missing
-    assert _gemv(fn, m=64, n=1024, ws_bytes=rewrite - 1) == 8            # too small
+    assert _gemv(fn, m=64, n=1024, ws_bytes=need - 1) == 8               # too small
     assert _gemv(fn, m=64, n=1024, ws=WS + 4, ws_bytes=need) == 4        # misaligned
     assert _gemv(fn, m=64, n=1024, ws=A + 0x2000000, ws_bytes=need) == 5  # over x
     assert _gemv(fn, m=64, n=1024, ws=A + 0x3000000 - 16, ws_bytes=need) == 5   # into y

@@ -1,12 +1,16 @@
-"""GPU parity of the bfloat16 product (tl_gemm_bf16: codes as exact bfloat16
--1/0/+1 on the matrix cores, each group's fp32 sums times its binary16 scale)
-against the fp64 oracle.  The kernel and the oracle read the same bfloat16
-activations (the oracle's rotation rounded to bfloat16), so the products are
-exact and only the fp32 sums round: relative L2 1e-5 and, element by element,
-1e-5 of the sum of |terms|.  End to end against the fp64 layer on the
-unrounded rotation, the bfloat16 rounding of the activations (8 significant
-bits, relative error <= 2^-9 per element) dominates; its derived size for
-random data is about 2^-9 / sqrt(3) = 1.1e-3, under the 2e-3 bar."""
+"""GPU parity of the bfloat16 product (tl_gemm_bf16: each activation row
+taken exactly to binary16 under a power-of-two factor, the binary16
+register-decode product, the factor undone on the outputs) against the fp64
+oracle.  The kernel and the oracle read the same bfloat16 activations (the
+oracle's rotation rounded to bfloat16), so the products are exact and only
+the fp32 sums round: relative L2 1e-5 and, element by element, 1e-5 of the
+sum of |terms|.  End to end against the fp64 layer on the unrounded rotation,
+the bfloat16 rounding of the activations (8 significant bits, relative error
+<= 2^-9 per element) dominates; its derived size for random data is about
+2^-9 / sqrt(3) = 1.1e-3, under the 2e-3 bar.  Rows far outside the binary16
+range (factors 2^-100 .. 2^100) keep the same bars, and where the rows are
+binary16 numbers the result equals tl_gemm's bit for bit (a power-of-two
+factor commutes with the fp32 rounding)."""
 import numpy as np
 import pytest
 import torch
@@ -111,3 +115,40 @@ def test_bf16_gemm_prefill_size_sampled_rows(gpu, shape):
     toks = np.concatenate([rng.choice(m, size=48, replace=False), [0, m - 1]])
     want = oracle.matvec(inp.codes[rows], inp.scales[rows], xr[toks])
     assert oracle.rel_l2(y[np.ix_(toks, rows)].astype(np.float64), want) < 1e-5
+
+
+@pytest.mark.parametrize("fmt", (tl.FMT_SLOT2, tl.FMT_TRIT5), ids=["slot2", "trit5"])
+def test_bf16_gemm_equals_binary16_product(gpu, fmt):
+    """Activations that are both bfloat16 and binary16 numbers: tl_gemm_bf16
+    gives tl_gemm's bits (fp32 outputs), whatever each row's factor."""
+    n, k, m = 700, 3072, 300
+    inp = _inputs(n, k, m, fmt, linear=21, cfg=3, outliers=True)
+    xr = oracle.round_bf16(oracle.rotate(inp.x, inp.signs))
+    xr[:20] *= 2.0 ** 6                    # rows whose factor differs
+    xr[20:40] *= 2.0 ** -6
+    xr[np.abs(xr) < 2.0 ** -14] = 0.0      # binary16 subnormals may not hold 8 bits
+    assert np.array_equal(xr.astype(np.float16).astype(np.float64), xr)
+    packed, scales = tl.pack(dev(inp.codes, gpu), fmt), dev(inp.scales, gpu)
+    a = host(tl.gemm_bf16(packed, scales, fmt, bf16(xr, gpu)))
+    b = host(tl.gemm(packed, scales, fmt, dev(xr.astype(np.float16), gpu)))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_bf16_gemm_rows_outside_binary16_range(gpu):
+    """Rows scaled by 2^100, 2^-100, 2^40, 2^-40 (bfloat16 numbers far outside
+    the binary16 range), an all-zero row and a row mixing 2^30 and 2^-30
+    elements: every row keeps the fp32 bar of its own magnitude."""
+    n, k, m = 512, 2048, 70
+    inp = _inputs(n, k, m, tl.FMT_SLOT2, linear=8)
+    xr = oracle.round_bf16(oracle.rotate(inp.x, inp.signs))
+    for r, f in enumerate([2.0 ** 100, 2.0 ** -100, 2.0 ** 40, 2.0 ** -40]):
+        xr[r] *= f
+    xr[4] = 0.0
+    xr[5, ::2] *= 2.0 ** 30
+    xr[5, 1::2] *= 2.0 ** -30
+    packed, scales = tl.pack(dev(inp.codes, gpu), tl.FMT_SLOT2), dev(inp.scales, gpu)
+    y = host(tl.gemm_bf16(packed, scales, tl.FMT_SLOT2, bf16(xr, gpu))).astype(np.float64)
+    want = oracle.matvec(inp.codes, inp.scales, xr)
+    assert np.all(y[4] == 0.0)
+    for r in [0, 1, 2, 3, 5, 6, m - 1]:
+        assert oracle.rel_l2(y[r], want[r]) < 1e-5, r

@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "tl_gemm": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p, i64, p]),
             "tl_gemm_noalloc": (i32, [p, p, i32, p, i64, i64, i64, p, i32, p]),
             "tl_gemm_workspace_bytes": (i64, [i64, i64, i64, i32]),
+            "tl_gemm_bf16_workspace_bytes": (i64, [i64, i64, i64, i32]),
             "tl_gemm_plan": (i32, [i64, i64, i64, p]),
             "tl_linear": (i32, [p, p, i32, p, p, i64, i64, i64, p, p, i32, p, i64, p]),
             "tl_quantize": (i32, [p, p, i64, i64, p, p, p]),
@@ -170,10 +171,18 @@ def quantize(w: torch.Tensor, signs: torch.Tensor):
 
 
 def gemm_workspace_bytes(m: int, n: int, k: int, fmt: int) -> int:
-    """Device workspace bytes tl_gemm / tl_gemm_bf16 / tl_linear need (0: none)."""
+    """Device workspace bytes tl_gemm / tl_linear need (0: none)."""
     b = int(lib().tl_gemm_workspace_bytes(m, n, k, fmt))
     if b < 0:
         raise TLError("tl_gemm_workspace_bytes", 2)
+    return b
+
+
+def gemm_bf16_workspace_bytes(m: int, n: int, k: int, fmt: int) -> int:
+    """Device workspace bytes tl_gemm_bf16 needs."""
+    b = int(lib().tl_gemm_bf16_workspace_bytes(m, n, k, fmt))
+    if b < 0:
+        raise TLError("tl_gemm_bf16_workspace_bytes", 2)
     return b
 
 
@@ -185,14 +194,14 @@ def gemm_plan(m: int, n: int, k: int) -> tuple[int, int, int]:
     return int(out[0]), int(out[1]), int(out[2])
 
 
-def _workspace(m, n, k, fmt, device, workspace):
+def _workspace(m, n, k, fmt, device, workspace, size=None):
     """(pointer, bytes) of the workspace a prefill call needs: the caller's
     uint8 tensor when given, else one from torch's allocator (None when the
     call needs none)."""
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, 1)
         return _ptr(workspace), workspace.numel(), workspace
-    need = gemm_workspace_bytes(m, n, k, fmt)
+    need = (size or gemm_workspace_bytes)(m, n, k, fmt)
     if need == 0:
         return _ptr(None), 0, None
     ws = torch.empty(need, dtype=torch.uint8, device=device)
@@ -224,7 +233,8 @@ def _linear(call: str, packed, scales, fmt, x_rot, out_dtype, out, x_dtype=torch
         _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
                         _stream(x_rot)))
     else:
-        wp, wb, _keep = _workspace(m, n, k, fmt, x_rot.device, workspace)
+        size = gemm_bf16_workspace_bytes if call == "tl_gemm_bf16" else None
+        wp, wb, _keep = _workspace(m, n, k, fmt, x_rot.device, workspace, size)
         _check(call, fn(_ptr(packed), _ptr(scales), fmt, _ptr(x_rot), m, n, k, _ptr(out), yd,
                         wp, wb, _stream(x_rot)))
     return out
@@ -244,8 +254,9 @@ def gemm_noalloc(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None) 
 
 def gemm_bf16(packed, scales, fmt, x_rot, out_dtype=torch.float32, out=None,
               workspace=None) -> torch.Tensor:
-    """The prefill product with bfloat16 rotated activations x_rot [M, K]:
-    codes as bfloat16 -1/0/+1 on the matrix cores, group scales in fp32."""
+    """The prefill product with bfloat16 rotated activations x_rot [M, K]: each
+    row taken exactly to binary16 under a power-of-two factor, then the
+    binary16 product (``workspace``: at least ``gemm_bf16_workspace_bytes``)."""
     return _linear("tl_gemm_bf16", packed, scales, fmt, x_rot, out_dtype, out,
                    x_dtype=torch.bfloat16, workspace=workspace)
 

@@ -111,7 +111,7 @@ __device__ __forceinline__ void decode8(uint32_t w, int h, ScaleSel sc, uint32_t
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4))) void gemm_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m, int64_t n,
     int64_t k, void* __restrict__ y, int y_f16, int tiles_n, int tiles, int t0, int chunk_a,
-    int splits, int chunk_b, float* __restrict__ ws) {
+    int splits, int chunk_b, float* __restrict__ ws, const float* __restrict__ row_scale) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const uint32_t st0 = uint32_t(uintptr_t((__attribute__((address_space(3))) uint8_t*)(smem)));
 
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
                 const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
                 const int64_t col = n0 + wn + 32 * j + (lane & 31);
                 if (row < m && col < n) {
-                    const float v = acc[i][j][r];
+                    const float v = row_scale ? acc[i][j][r] * row_scale[row] : acc[i][j][r];
                     if (y_f16)
                         reinterpret_cast<__half*>(y)[row * n + col] = __float2half_rn(v);
                     else
@@ -474,7 +474,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 // register of wave tid / 64 at the same place as there.
 __global__ __launch_bounds__(kThreads) void gemm_slot2_reduce(const float* __restrict__ ws,
                                                               int64_t m, int64_t n, void* __restrict__ y,
-                                                              int y_f16, int tiles_n, int t0, int splits) {
+                                                              int y_f16, int tiles_n, int t0, int splits,
+                                                              const float* __restrict__ row_scale) {
     const int tt = int(blockIdx.x) / kRegs, e = int(blockIdx.x) % kRegs;
     const int tile = t0 + tt;
     const int64_t m0 = int64_t(tile / tiles_n) * BM;
@@ -488,6 +489,7 @@ __global__ __launch_bounds__(kThreads) void gemm_slot2_reduce(const float* __res
     const int64_t row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
     const int64_t col = n0 + wn + 32 * j + (lane & 31);
     if (row < m && col < n) {
+        if (row_scale) sum *= row_scale[row];
         if (y_f16)
             reinterpret_cast<__half*>(y)[row * n + col] = __float2half_rn(sum);
         else
@@ -543,7 +545,7 @@ int64_t gemm_slot2_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16, void* ws,
-                             int64_t ws_bytes, hipStream_t stream) {
+                             int64_t ws_bytes, hipStream_t stream, const float* row_scale) {
     if (!gemm_slot2_fits(m, n, k)) return hipErrorInvalidValue;
     const Gemm2Plan pl = gemm_slot2_plan(m, n, k);
     const int64_t items = (pl.tiles - pl.t0) * pl.splits;
@@ -556,12 +558,12 @@ hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, cons
     const int64_t chunk_a = (pl.t0 + 7) / 8, chunk_b = (items + 7) / 8;
     hipLaunchKernelGGL(gemm_slot2_kernel, dim3(unsigned(8 * (chunk_a + chunk_b))), dim3(kThreads),
                        size_t(kLds), stream, packed, scales, x, m, n, k, y, y_f16, int(tiles_n),
-                       int(pl.tiles), int(pl.t0), int(chunk_a), pl.splits, int(chunk_b), part);
+                       int(pl.tiles), int(pl.t0), int(chunk_a), pl.splits, int(chunk_b), part, row_scale);
     if (pl.splits > 1) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(gemm_slot2_reduce, dim3(unsigned(kRegs * (pl.tiles - pl.t0))),
                            dim3(kThreads), 0, stream, part, m, n, y, y_f16, int(tiles_n),
-                           int(pl.t0), pl.splits);
+                           int(pl.t0), pl.splits, row_scale);
     }
     return hipGetLastError();
 }

@@ -137,6 +137,11 @@ int64_t tl_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt) {
     return tl::gemm_workspace_bytes(M, N, K, fmt, false);
 }
 
+int64_t tl_gemm_bf16_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t fmt) {
+    if (!layer_shape_ok(M, N, K) || !known_fmt(fmt) || !tl::gemm_fits(M, N, K)) return -1;
+    return tl::gemm_workspace_bytes(M, N, K, fmt, true);
+}
+
 tl_status tl_gemm_plan(int64_t M, int64_t N, int64_t K, int64_t* out) {
     if (!out) return TL_ERR_NULL;
     if (!layer_shape_ok(M, N, K) || !tl::gemm_fits(M, N, K)) return TL_ERR_SHAPE;

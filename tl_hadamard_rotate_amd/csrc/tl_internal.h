@@ -71,7 +71,8 @@ hipError_t launch_gemv_bit1(const uint8_t* packed, const uint16_t* scales, const
 // Prefill GEMM of the 2-bit-slot packing with the weights decoded in
 // registers; usable when gemm_slot2_fits(m, n, k).  Its launch plan: `tiles`
 // output tiles, tiles [0, t0) computed whole, each later one split along K
-// into `splits` parts whose fp32 partial sums need workspace.
+// into `splits` parts whose fp32 partial sums need workspace.  row_scale
+// (optional): every output of row m is multiplied by row_scale[m].
 bool gemm_slot2_fits(int64_t m, int64_t n, int64_t k);
 struct Gemm2Plan {
     int64_t tiles, t0;
@@ -81,26 +82,24 @@ Gemm2Plan gemm_slot2_plan(int64_t m, int64_t n, int64_t k);
 int64_t gemm_slot2_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemm_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                              int64_t m, int64_t n, int64_t k, void* y, int y_f16, void* ws,
-                             int64_t ws_bytes, hipStream_t stream);
-// The bfloat16-activation product of the 2-bit-slot packing
-hipError_t launch_gemm_bf16_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
-                                  int64_t m, int64_t n, int64_t k, void* y, int y_f16,
-                                  hipStream_t stream);
+                             int64_t ws_bytes, hipStream_t stream, const float* row_scale = nullptr);
 // Rotate real-valued weight rows and round them to ternary g128
 hipError_t launch_quantize(const float* w, const int8_t* signs, int64_t n, int64_t k,
                            int8_t* codes, uint16_t* scales, hipStream_t stream);
 // Prefill products (fp16 or bfloat16 activations) of any packing.  Dense
 // trits and 1-bit codes are first rewritten as 2-bit slots into the start of
-// the caller's workspace; the K-split partial sums follow at the next
-// 256-byte boundary.  gemm_workspace_bytes gives the bytes a call needs (0:
-// none); gemm_fits whether the shape is supported at all.
+// the caller's workspace; bfloat16 activations then get their binary16 copy
+// and row scales; the K-split partial sums follow, each part at a 256-byte
+// boundary.  gemm_workspace_bytes gives the bytes a call needs (0: none);
+// gemm_fits whether the shape is supported at all.
 bool gemm_fits(int64_t m, int64_t n, int64_t k);
 int64_t gemm_workspace_bytes(int64_t m, int64_t n, int64_t k, int fmt, bool bf16);
 hipError_t launch_gemm(const uint8_t* packed, const uint16_t* scales, int fmt,
                        const uint16_t* x, int64_t m, int64_t n, int64_t k,
                        void* y, int y_f16, void* ws, int64_t ws_bytes, hipStream_t stream);
-// The product with bfloat16 activations: codes as bfloat16 -1/0/+1 on the
-// matrix cores, each group's fp32 sums times the binary16 scale
+// The product with bfloat16 activations: each row scaled by a power of two
+// and converted exactly to binary16, the binary16 product, the power of two
+// undone on the outputs
 hipError_t launch_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int fmt,
                             const uint16_t* x, int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                             void* ws, int64_t ws_bytes, hipStream_t stream);
