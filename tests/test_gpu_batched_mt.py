@@ -1,10 +1,12 @@
 """GPU parity of the few-token decode GEMV with 2-bit slots (tl_gemv at
 2 <= M <= 16): tokens ride on the matrix-core rows, 8 rows of weights per
-unit, 8 tokens per pass (fewer when their activation images do not fit in
-LDS), one launch per pass.  Shapes cover a ragged last unit of rows, fewer
-rows than a unit, one 1024-block, partial passes (M not a multiple of the
-pass), two passes, passes of 2 at K = 17408, and a row count that needs
-several row chunks per workgroup.  Every output (or, at the largest N, a
+unit, up to 8 tokens per workgroup (fewer when their activation images do
+not fit in LDS); more tokens form a second group in the same launch, paired
+workgroups taking the same rows.  Shapes cover a ragged last unit of rows,
+fewer rows than a unit, one 1024-block, a partial group (M not a multiple of
+the group), two groups (also with fewer row sets than a multiple of 8, so
+that the paired grid has idle padding), groups of 2 at K = 17408, and a row
+count that needs several row chunks per workgroup.  Every output (or, at the largest N, a
 sample of rows in every tile) is compared with the oracle's product on the
 same binary16 activations (exact products, fp32 sums: relative L2 < 1e-5
 per token) and with the fp64 layer (2e-3)."""
@@ -87,7 +89,7 @@ def test_gemv_few_tokens_scale_per_token(gpu):
 
 def test_gemv_few_tokens_deterministic_and_token_independent(gpu):
     """Two calls give the same bits; a token's outputs do not depend on the
-    other tokens of its pass (token 0 next to zero partners equals token 0
+    other tokens of its group (token 0 next to zero partners equals token 0
     next to random ones, at M = 8 and at M = 2)."""
     m, n, k = 8, 2048, 5120
     inp = synth.linear_inputs(n, k, m, cfg=3, linear=5, outliers=True)

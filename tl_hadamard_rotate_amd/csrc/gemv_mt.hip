@@ -32,9 +32,12 @@
 // four tokens' partial sums of their row and chunk to LDS; the sums are added
 // over the chunks in ascending order (bitwise deterministic).
 //
-// Tokens are processed in passes of MT (8, or 4 or 2 when 8 tokens' images do
-// not fit in LDS), one launch per pass; a second pass streams the weights again
-// (from the L2 cache in practice: a workgroup's slice is tens of KB).
+// A workgroup holds the images of MT tokens (8, or 4 or 2 when 8 tokens'
+// images do not fit in LDS).  With more tokens than that (at most 2 MT), the
+// tokens form two groups and both run in one launch: workgroups b and b + 8
+// (the same XCD) take the same rows, one group each, so that the second read
+// of their weights finds them in that XCD's L2 cache; every workgroup then
+// owns twice the rows it would with one group.
 //
 // Work split and memory pipeline as at M = 1: one 1024-thread workgroup per CU
 // owns a contiguous slice of rows; a wave takes a contiguous run of pair units
@@ -70,8 +73,9 @@ __host__ __device__ constexpr int rec_tok_bytes(int nb) { return nb * 4 * kRecBy
 
 template <int FL, int MT>
 __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
-    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int mt, int64_t n,
-    int64_t k, int row_base, int row_rem, int rows_per_chunk, void* __restrict__ y, int y_f16) {
+    const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int m, int64_t n,
+    int64_t k, int sets, int tgroups, int row_base, int row_rem, int rows_per_chunk,
+    void* __restrict__ y, int y_f16) {
     constexpr int V = MT < 4 ? MT : 4;       // tokens per D lane
     // Where the groups' sums of x come from: at 8 tokens from the matrix cores
     // once per chunk (the image build, which runs on every wave, is then the
@@ -96,7 +100,17 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const int h = q - 2 * s;                 // lanes holding tokens 4h .. 4h + 3 of D
     const bool dlane = (q >> 1) == s && 4 * h < MT;
 
-    const int bid = int(blockIdx.x);
+    // row set and token group of this workgroup: with two groups, workgroups
+    // b and b + 8 (b % 16 < 8) take row set (b % 8) + 8 (b / 16), groups 0 and 1
+    int bid = int(blockIdx.x), grp = 0;
+    if (tgroups == 2) {
+        grp = (bid >> 3) & 1;
+        bid = (bid & 7) | ((bid >> 4) << 3);
+    }
+    if (bid >= sets) return;   // padding of the paired grid (whole workgroup)
+    const int mt = min(MT, m - grp * MT);
+    x += int64_t(grp) * MT * k;
+    const int64_t y_tok0 = int64_t(grp) * MT;   // first output row of the group
     const int64_t r0 = int64_t(bid) * row_base + min(bid, row_rem);
     const int rows = row_base + (bid < row_rem ? 1 : 0);
     const int64_t row_bytes = k / 4;
@@ -254,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
                 const float4 p = pr[c4];
                 v = (((v + p.x) + p.y) + p.z) + p.w;
             }
-            const int64_t o = int64_t(tk) * n + r0 + rc0 + r;
+            const int64_t o = (y_tok0 + tk) * n + r0 + rc0 + r;
             if (y_f16)
                 reinterpret_cast<__half*>(y)[o] = __float2half_rn(v);
             else
@@ -339,7 +353,9 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
 
 struct MtPlan {
     unsigned grid;
-    int mt;        // tokens per pass
+    int sets;      // row sets (workgroups per token group)
+    int groups;    // token groups (1 or 2)
+    int mt;        // tokens per group
     int rpc;       // rows per chunk
     int steps;     // steps per wave and row chunk
     size_t lds;
@@ -349,7 +365,7 @@ size_t fixed_lds(int64_t nb, int mt) {
     return size_t(mt) * size_t(tok_stride(int(nb))) + size_t(mt) * size_t(rec_tok_bytes(int(nb)));
 }
 
-// tokens per pass: 8, or fewer when 8 images do not fit beside one row of
+// tokens per group: 8, or fewer when 8 images do not fit beside one row of
 // partial sums; 0 when not even 2 fit
 int pick_mt(int64_t m, int64_t k) {
     const int64_t nb = k / kBlock;
@@ -367,14 +383,20 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
     MtPlan p{};
     p.mt = pick_mt(m, k);
     if (p.mt == 0) return p;
-    // at least a unit of rows per workgroup when there are few rows
+    p.groups = int((m + p.mt - 1) / p.mt);
+    // at least a unit of rows per workgroup when there are few rows; with two
+    // groups, half the CUs per group and the grid padded to whole 16s (the
+    // pairing of workgroups b and b + 8)
     const int64_t units = (n + kUnitRows - 1) / kUnitRows;
-    const int64_t grid = units < cu_count() ? units : cu_count();
-    const int64_t rows = (n + grid - 1) / grid;
+    const int64_t cus = p.groups == 2 ? cu_count() / 2 : cu_count();
+    const int64_t sets = units < cus ? units : cus;
+    const int64_t grid = p.groups == 2 ? 16 * ((sets + 7) / 8) : sets;
+    const int64_t rows = (n + sets - 1) / sets;
     const size_t fixed = fixed_lds(nb, p.mt);
     int64_t rpc = int64_t((kLdsLimit - fixed) / (size_t(4 * nb) * p.mt * 4));
     if (rpc > rows) rpc = rows;
     p.grid = unsigned(grid);
+    p.sets = int(sets);
     p.rpc = int(rpc);
     const int64_t g = (rpc + kUnitRows - 1) / kUnitRows;
     p.steps = int((2 * nb * g + kWaves - 1) / kWaves);
@@ -384,34 +406,34 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
 
 template <int FL, int MT>
 hipError_t launch_fl(const MtPlan& p, const uint8_t* packed, const uint16_t* scales,
-                     const uint16_t* x, int mt, int64_t n, int64_t k, void* y, int y_f16,
+                     const uint16_t* x, int m, int64_t n, int64_t k, void* y, int y_f16,
                      hipStream_t stream) {
-    const int base = int(n / p.grid), rem = int(n % p.grid);
+    const int base = int(n / p.sets), rem = int(n % p.sets);
     const hipError_t e =
         allow_lds(reinterpret_cast<const void*>(gemv_mt_slot2_kernel<FL, MT>), int(kLdsLimit));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gemv_mt_slot2_kernel<FL, MT>), dim3(p.grid), dim3(kThreads), p.lds, stream,
-                       packed, scales, x, mt, n, k, base, rem, p.rpc, y, y_f16);
+                       packed, scales, x, m, n, k, p.sets, p.groups, base, rem, p.rpc, y, y_f16);
     return hipGetLastError();
 }
 
-// one pass: mt <= MT tokens starting at x, outputs starting at y
+// every token: one or two groups of at most MT tokens
 template <int MT>
 hipError_t launch_pass(const MtPlan& p, const uint8_t* packed, const uint16_t* scales,
-                       const uint16_t* x, int mt, int64_t n, int64_t k, void* y, int y_f16,
+                       const uint16_t* x, int m, int64_t n, int64_t k, void* y, int y_f16,
                        hipStream_t stream) {
     // up to 7 steps a slot: one flight; up to 4 flights of kRingMaxFLMt: a
     // ring; beyond, flights of 7 (8 does not fit the registers)
     if (p.steps > 7 && p.steps <= kRingMaxFLMt * (kRingFlightsMt + 1))
-        return launch_fl<kRingMaxFLMt, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
+        return launch_fl<kRingMaxFLMt, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
     switch (p.steps) {
-        case 1: return launch_fl<1, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        case 2: return launch_fl<2, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        case 3: return launch_fl<3, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        case 4: return launch_fl<4, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        case 5: return launch_fl<5, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        case 6: return launch_fl<6, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
-        default: return launch_fl<7, MT>(p, packed, scales, x, mt, n, k, y, y_f16, stream);
+        case 1: return launch_fl<1, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 2: return launch_fl<2, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 3: return launch_fl<3, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 4: return launch_fl<4, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 5: return launch_fl<5, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 6: return launch_fl<6, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        default: return launch_fl<7, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
     }
 }
 
@@ -421,9 +443,9 @@ bool gemv_mt_slot2_fits(int64_t m, int64_t n, int64_t k) {
     if (m < 2 || m > 16 || k < kBlock || k % kBlock != 0) return false;
     const MtPlan p = mt_plan(m, n, k);
     if (p.mt == 0 || p.rpc < 1 || p.lds > kLdsLimit) return false;
-    // at most two passes; 32-bit buffer offsets within a workgroup's slice
-    const int64_t rows = (n + p.grid - 1) / p.grid;
-    return (m + p.mt - 1) / p.mt <= 2 && rows * (k / 4) < (int64_t(1) << 31);
+    // at most two token groups; 32-bit buffer offsets within a workgroup's slice
+    const int64_t rows = (n + p.sets - 1) / p.sets;
+    return p.groups <= 2 && rows * (k / 4) < (int64_t(1) << 31);
 }
 
 hipError_t launch_gemv_mt_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
@@ -431,22 +453,11 @@ hipError_t launch_gemv_mt_slot2(const uint8_t* packed, const uint16_t* scales, c
                                 hipStream_t stream) {
     if (!gemv_mt_slot2_fits(m, n, k)) return hipErrorInvalidValue;
     const MtPlan p = mt_plan(m, n, k);
-    const int64_t y_elem = y_f16 ? 2 : 4;
-    // one launch per pass of p.mt tokens (a second pass finds the weights in
-    // the L2 cache)
-    for (int64_t m0 = 0; m0 < m; m0 += p.mt) {
-        const int mt = int(m - m0 < p.mt ? m - m0 : p.mt);
-        const uint16_t* xs = x + m0 * k;
-        void* ys = static_cast<uint8_t*>(y) + m0 * n * y_elem;
-        hipError_t e;
-        switch (p.mt) {
-            case 2: e = launch_pass<2>(p, packed, scales, xs, mt, n, k, ys, y_f16, stream); break;
-            case 4: e = launch_pass<4>(p, packed, scales, xs, mt, n, k, ys, y_f16, stream); break;
-            default: e = launch_pass<8>(p, packed, scales, xs, mt, n, k, ys, y_f16, stream); break;
-        }
-        if (e != hipSuccess) return e;
+    switch (p.mt) {
+        case 2: return launch_pass<2>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
+        case 4: return launch_pass<4>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
+        default: return launch_pass<8>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
     }
-    return hipSuccess;
 }
 
 }  // namespace tl
