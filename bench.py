@@ -7,8 +7,8 @@ with the signed 1024-block Hadamard transform, binary16 output) then down,
 whose input is the gate part of that output (the SwiGLU between them in a
 model is outside the library).  Each launch is the fused rotation + ternary
 product kernel.  Inputs are seeded synthetic tensors with the workload's
-distributions.  With --fmt trit5 the step is the three projections as
-separate tl_linear launches.
+distributions.  --fmt trit5 runs the same step with the dense trit
+packing.
 
 Timing.  Each step is captured once in a HIP graph; the weights are replicated
 into --copies distinct buffers (one graph per copy) and the timed loop cycles
@@ -26,9 +26,9 @@ traffic comes from the rocprofv3 counter summary under profiles/ and is
 reported only while the kernel source is the one those counters were taken
 from.
 
-Extras: each launch of the step, the step as one tl_linear_chain launch,
-the three projections as separate launches (and the GEMVs alone), the other
-packing, the 64-layer weight stream (one chain launch per token with
+Extras: each launch of the step, the step as one tl_linear_chain launch
+(2-bit slots), the three projections as separate launches (and the GEMVs
+alone), the step and the separate launches with the other packing, the 64-layer weight stream (one chain launch per token with
 dependent and with independent inputs, and one launch per linear or per
 input), the prefill GEMM sweep (and its bfloat16 variant at M = 4096),
 batched decode over the attention projections, the rotation at prefill size,
@@ -61,7 +61,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 matrix peak
 STEP_LINEARS = ("gate", "up", "down")
 FMT_NAMES = {"trit5": 0, "slot2": 1, "bit1": 2}
 KERNEL_SRC = {0: "gemv_trit5.hip", 1: "gemv_m1.hip"}
-PROFILE_NAME = {0: "linear_m1_trit5_decode_mlp", 1: "linear_m1_slot2_decode_step"}
+PROFILE_NAME = {0: "linear_m1_trit5_decode_step", 1: "linear_m1_slot2_decode_step"}
 
 
 def log(msg: str) -> None:
@@ -573,18 +573,18 @@ def read_floor(torch, tl, dev, reps=20) -> int:
 
 def profile_pass(torch, tl, synth, dev, fmt) -> int:
     """Kernels for the HBM-counter runs: the calibration copy (256 MiB read and
-    256 MiB written per launch), then, with 2-bit slots, 10 eager steps (the
-    timed step: tl_linear on gate|up, then on down), then 10 eager decode
-    steps as separate launches per projection (tl_linear, and tl_gemv alone);
-    weights cycled over 8 copies."""
+    256 MiB written per launch), then, with 2-bit slots or dense trits, 10
+    eager steps (the timed step: tl_linear on gate|up, then on down), then 10
+    eager decode steps as separate launches per projection (tl_linear, and
+    tl_gemv alone); weights cycled over 8 copies."""
     src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    if fmt == 1:
-        steps, _ = build_mlp_step(torch, tl, synth, dev, 8)
+    if fmt in (0, 1):
+        steps, _ = build_mlp_step(torch, tl, synth, dev, 8, fmt)
         for i in range(10):
             for fn in steps[i % 8]:
                 fn()
@@ -730,13 +730,13 @@ def build_chain_step(torch, tl, synth, dev, copies):
     return chains, step_bytes
 
 
-def build_mlp_step(torch, tl, synth, dev, copies):
+def build_mlp_step(torch, tl, synth, dev, copies, fmt=1):
     """The decode step as two tl_linear launches per weight copy: gate|up (the
     two projections that read the same input, rows concatenated: one rotation,
     binary16 output) then down on the gate part of that output (the SwiGLU
     between them in a model is outside this library; stream order makes down
-    wait for gate|up).  Returns per-copy lists of the two launches (callables)
-    and the step's algorithmic bytes."""
+    wait for gate|up), with packing fmt.  Returns per-copy lists of the two
+    launches (callables) and the step's algorithmic bytes."""
     import numpy as np
 
     ins = {}
@@ -747,9 +747,9 @@ def build_mlp_step(torch, tl, synth, dev, copies):
     g, u, d = ins["gate"], ins["up"], ins["down"]
     kg, ng = synth.SHAPES["gate"]
     kd, nd = synth.SHAPES["down"]
-    gu_packed = tl.pack(torch.from_numpy(np.concatenate([g.codes, u.codes])).to(dev), 1)
+    gu_packed = tl.pack(torch.from_numpy(np.concatenate([g.codes, u.codes])).to(dev), fmt)
     gu_scales = torch.from_numpy(np.concatenate([g.scales, u.scales])).to(dev)
-    dn_packed = tl.pack(torch.from_numpy(d.codes).to(dev), 1)
+    dn_packed = tl.pack(torch.from_numpy(d.codes).to(dev), fmt)
     dn_scales = torch.from_numpy(d.scales).to(dev)
     x = torch.from_numpy(g.x).to(dev)
     s_gu, s_dn = torch.from_numpy(g.signs).to(dev), torch.from_numpy(d.signs).to(dev)
@@ -763,11 +763,11 @@ def build_mlp_step(torch, tl, synth, dev, copies):
         pg, sg = (gu_packed, gu_scales) if c == 0 else (gu_packed.clone(), gu_scales.clone())
         pd, sd = (dn_packed, dn_scales) if c == 0 else (dn_packed.clone(), dn_scales.clone())
         steps.append([
-            (lambda pg=pg, sg=sg: tl.linear(pg, sg, 1, x, s_gu, out_dtype=torch.float16, out=y_gu,
-                                            x_rot=xr_gu)),
-            (lambda pd=pd, sd=sd: tl.linear(pd, sd, 1, x_dn, s_dn, out=y_dn, x_rot=xr_dn))])
-    launch_bytes = [linear_bytes(2 * ng, kg, 1, 1) - 2 * ng * 2,    # binary16 output
-                    linear_bytes(nd, kd, 1, 1)]
+            (lambda pg=pg, sg=sg: tl.linear(pg, sg, fmt, x, s_gu, out_dtype=torch.float16,
+                                            out=y_gu, x_rot=xr_gu)),
+            (lambda pd=pd, sd=sd: tl.linear(pd, sd, fmt, x_dn, s_dn, out=y_dn, x_rot=xr_dn))])
+    launch_bytes = [linear_bytes(2 * ng, kg, 1, fmt) - 2 * ng * 2,    # binary16 output
+                    linear_bytes(nd, kd, 1, fmt)]
     return steps, launch_bytes
 
 
@@ -952,33 +952,35 @@ def main(argv=None) -> int:
         return read_floor(torch, tl, dev)
 
     extra = {}
+    # the step: gate|up then down, two fused rotate + GEMV launches
+    log(f"building the step (gate|up, down), fmt={args.fmt}, copies={args.copies}")
+    steps, launch_bytes = build_mlp_step(torch, tl, synth, dev, args.copies, fmt)
+    with torch.cuda.stream(stream):
+        step_graphs = capture(torch, lambda c: [fn() for fn in steps[c]], args.copies, stream)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    ms = timed_replays(torch, step_graphs, args.steps, args.warmup, stream) / args.steps
+    sbytes = sum(launch_bytes)
+    launches = 2
+    per = per_launch_times_us(torch, steps, max(args.steps, 2 * args.copies), stream)
+    kern_us = sum(per) / len(per)
+    per_launch = sbytes / len(per)
+    kname = ("gemv_m1_slot2_kernel<FL, true> (tl_linear, rotation fused): gate|up and down"
+             if fmt == 1 else
+             "gemv_trit5_kernel<1, true, true> (tl_linear, rotation fused): gate|up and down")
+    workload = ("decode step M=1 over the 27B-class MLP projections: gate|up (K=5120, "
+                "N=2x17408, rows concatenated, one signed 1024-block Hadamard rotation of the "
+                "input, binary16 output) then down (K=17408, N=5120) on the gate part of that "
+                "output (the SwiGLU between them is outside the library), each one fused "
+                "rotation + ternary g128 GEMV launch (tl_linear); binary16 activations, fp32 "
+                "accumulation")
+    extra["step_launches"] = [
+        {"linear": "gate|up", "us": round(per[0], 3), "bytes": launch_bytes[0],
+         "GBs": round(launch_bytes[0] / (per[0] * 1e-6) / 1e9, 1)},
+        {"linear": "down", "us": round(per[1], 3), "bytes": launch_bytes[1],
+         "GBs": round(launch_bytes[1] / (per[1] * 1e-6) / 1e9, 1)}]
+    del step_graphs, steps
+    torch.cuda.empty_cache()
     if fmt == 1:
-        # the step: gate|up then down, two fused rotate + GEMV launches
-        log(f"building the step (gate|up, down), copies={args.copies}")
-        steps, launch_bytes = build_mlp_step(torch, tl, synth, dev, args.copies)
-        with torch.cuda.stream(stream):
-            step_graphs = capture(torch, lambda c: [fn() for fn in steps[c]], args.copies, stream)
-        log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-        ms = timed_replays(torch, step_graphs, args.steps, args.warmup, stream) / args.steps
-        sbytes = sum(launch_bytes)
-        launches = 2
-        per = per_launch_times_us(torch, steps, max(args.steps, 2 * args.copies), stream)
-        kern_us = sum(per) / len(per)
-        per_launch = sbytes / len(per)
-        kname = "gemv_m1_slot2_kernel<FL, true> (tl_linear, rotation fused): gate|up and down"
-        workload = ("decode step M=1 over the 27B-class MLP projections: gate|up (K=5120, "
-                    "N=2x17408, rows concatenated, one signed 1024-block Hadamard rotation of the "
-                    "input, binary16 output) then down (K=17408, N=5120) on the gate part of that "
-                    "output (the SwiGLU between them is outside the library), each one fused "
-                    "rotation + ternary g128 GEMV launch (tl_linear); binary16 activations, fp32 "
-                    "accumulation")
-        extra["step_launches"] = [
-            {"linear": "gate|up", "us": round(per[0], 3), "bytes": launch_bytes[0],
-             "GBs": round(launch_bytes[0] / (per[0] * 1e-6) / 1e9, 1)},
-            {"linear": "down", "us": round(per[1], 3), "bytes": launch_bytes[1],
-             "GBs": round(launch_bytes[1] / (per[1] * 1e-6) / 1e9, 1)}]
-        del step_graphs, steps
-        torch.cuda.empty_cache()
         # the same step as one chain launch (down waits for gate|up on the device)
         log("the step as one tl_linear_chain launch")
         chains, cbytes = build_chain_step(torch, tl, synth, dev, args.copies)
@@ -992,8 +994,6 @@ def main(argv=None) -> int:
                                   "step_GBs": round(cbytes / (cms * 1e-3) / 1e9, 1)}
         del cg, chains
         torch.cuda.empty_cache()
-    else:
-        ms = kern_us = per_launch = None
     # the three projections as separate launches (tl_linear per projection)
     log(f"separate launches per projection, fmt={args.fmt}")
     lins = build_step_inputs(torch, tl, synth, dev, fmt, args.copies)
@@ -1011,20 +1011,6 @@ def main(argv=None) -> int:
         "step_GBs": round(sep_bytes / (sep_ms * 1e-3) / 1e9, 1),
         "gemv_alone_avg_launch_us": round(g_us, 3),
         "gemv_alone_GBs": round(g_bytes / (g_us * 1e-6) / 1e9, 1)}
-    if fmt != 1:
-        # dense trits: the three separate launches are the step
-        ms, sbytes, launches = sep_ms, sep_bytes, 3
-        sep_steps = [[(lambda l=l, c=c: tl.linear(l["packs"][c], l["scales"][c], fmt, l["x"],
-                                                  l["signs"], out=l["y"], x_rot=l["x_rot"]))
-                      for l in lins] for c in range(args.copies)]
-        per = per_launch_times_us(torch, sep_steps, reps, stream)
-        kern_us = sum(per) / len(per)
-        per_launch = sum(linear_bytes(l["n"], l["k"], 1, fmt) for l in lins) / 3.0
-        kname = "gemv_trit5_kernel (tl_linear, rotation fused)"
-        workload = ("decode step M=1 over 27B-class MLP projections gate/up (K=5120, N=17408) and "
-                    "down (K=17408, N=5120): signed 1024-block Hadamard rotation + ternary g128 "
-                    "GEMV per projection (tl_linear, one launch each); binary16 activations, fp32 "
-                    "accumulation")
     del sep_graphs, gemv_graphs, lins
     torch.cuda.empty_cache()
     value = sbytes / (ms * 1e-3) / 1e9
@@ -1045,6 +1031,17 @@ def main(argv=None) -> int:
 
     if not args.no_extra:
         other = 1 - fmt
+        oname = "slot2" if other == 1 else "trit5"
+        log(f"the step (gate|up, down) with fmt={oname}")
+        steps2, lb2 = build_mlp_step(torch, tl, synth, dev, args.copies, other)
+        with torch.cuda.stream(stream):
+            sg2 = capture(torch, lambda c: [fn() for fn in steps2[c]], args.copies, stream)
+        ms3 = timed_replays(torch, sg2, args.steps, args.warmup, stream) / args.steps
+        extra["other_format_step"] = {"fmt": oname, "launches": 2, "ms_per_step": round(ms3, 5),
+                                      "step_bytes": sum(lb2),
+                                      "step_GBs": round(sum(lb2) / (ms3 * 1e-3) / 1e9, 1)}
+        del sg2, steps2
+        torch.cuda.empty_cache()
         lins2 = build_step_inputs(torch, tl, synth, dev, other, args.copies)
         with torch.cuda.stream(stream):
             sg = capture(torch, lambda c: step_fn(tl, lins2, other, c), args.copies, stream)

@@ -1,7 +1,8 @@
 """GPU parity on the launch plans the benchmark times, at the workloads' full
 sizes: the prefill GEMM at M = 512, 2048, 4096 (whole tiles and K-split
 tiles), the batched decode GEMV over the attention projections with
-outliers, the fused M = 1 path on the o projection, a captured graph of a
+outliers, the fused M = 1 path on the o projection, the decode step as the
+benchmark runs it (gate|up concatenated, then down), a captured graph of a
 whole layer, and guard bands around every output of ragged shapes.
 
 Full-size outputs are checked on samples the oracle computes one by one:
@@ -196,6 +197,37 @@ def test_linear_o_projection(gpu, fmt, out_dtype):
     assert oracle.rel_l2(y, oracle.matvec(inp.codes, inp.scales, xr)) < (
         1e-5 if out_dtype == torch.float32 else 2e-3)
     assert oracle.rel_l2(y, oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)) < 2e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
+def test_decode_step_as_benchmarked(gpu, fmt):
+    """The benchmark's decode step at M = 1: tl_linear on gate|up (rows
+    concatenated, N = 34816, K = 5120, binary16 output), then tl_linear on
+    down (K = 17408) reading the gate part of that output.  Every output of
+    both launches against the oracle: on the binary16 rotated activations
+    each launch read, and on the fp64 layer of its own input."""
+    ins = {name: synth.linear_inputs(synth.SHAPES[name][1], synth.SHAPES[name][0], 1, cfg=2,
+                                     linear=synth.LINEAR_ID[name])
+           for name in ("gate", "up", "down")}
+    g, u, d = ins["gate"], ins["up"], ins["down"]
+    codes_gu = np.concatenate([g.codes, u.codes])
+    scales_gu = np.concatenate([g.scales, u.scales])
+    kg, kd = synth.SHAPES["gate"][0], synth.SHAPES["down"][0]
+    y_gu = torch.empty((1, codes_gu.shape[0]), dtype=torch.float16, device=gpu)
+    xr_gu = torch.empty((1, kg), dtype=torch.float16, device=gpu)
+    xr_dn = torch.empty((1, kd), dtype=torch.float16, device=gpu)
+    tl.linear(tl.pack(dev(codes_gu, gpu), fmt), dev(scales_gu, gpu), fmt, dev(g.x, gpu),
+              dev(g.signs, gpu), out_dtype=torch.float16, out=y_gu, x_rot=xr_gu)
+    y_dn = tl.linear(tl.pack(dev(d.codes, gpu), fmt), dev(d.scales, gpu), fmt, y_gu[:, :kd],
+                     dev(d.signs, gpu), x_rot=xr_dn)
+    got_gu = host(y_gu).astype(np.float64)
+    # binary16 outputs: the fp32 sums rounded once more (half an ulp)
+    assert oracle.rel_l2(got_gu, oracle.matvec(codes_gu, scales_gu, host(xr_gu))) < 1e-3
+    assert oracle.rel_l2(got_gu, oracle.linear(g.x, g.signs, codes_gu, scales_gu)) < 2e-3
+    x_dn = host(y_gu)[:, :kd]
+    got_dn = host(y_dn).astype(np.float64)
+    assert oracle.rel_l2(got_dn, oracle.matvec(d.codes, d.scales, host(xr_dn))) < 1e-5
+    assert oracle.rel_l2(got_dn, oracle.linear(x_dn, d.signs, d.codes, d.scales)) < 2e-3
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
