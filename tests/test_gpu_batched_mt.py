@@ -6,7 +6,9 @@ workgroups taking the same rows.  Shapes cover a ragged last unit of rows,
 fewer rows than a unit, one 1024-block, a partial group (M not a multiple of
 the group), two groups (also with fewer row sets than a multiple of 8, so
 that the paired grid has idle padding), groups of 2 at K = 17408, and a row
-count that needs several row chunks per workgroup.  Every output (or, at the largest N, a
+count that needs several row chunks per workgroup.  The 1-bit packing runs
+the same kernel (each 16 bits of codes spread into a 2-bit-slot word) and
+takes the same shapes.  Every output (or, at the largest N, a
 sample of rows in every tile) is compared with the oracle's product on the
 same binary16 activations (exact products, fp32 sums: relative L2 < 1e-5
 per token) and with the fp64 layer (2e-3)."""
@@ -21,6 +23,8 @@ import tl_hadamard_rotate_amd as tl
 pytestmark = pytest.mark.gpu
 
 SLOT2 = tl.FMT_SLOT2
+BIT1 = tl.FMT_BIT1
+FMTS = {"slot2": SLOT2, "bit1": BIT1}
 
 
 def dev(a, device):
@@ -42,11 +46,13 @@ def _per_token_err(y, want):
     (9, 130, 1024), (13, 777, 6144), (16, 4097, 2048), (2, 1024, 17408), (3, 333, 17408),
     (4, 515, 17408), (6, 2051, 4096)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16], ids=["f32", "f16"])
-def test_gemv_few_tokens_every_output(gpu, m, n, k, out_dtype):
-    inp = synth.linear_inputs(n, k, m, cfg=3, linear=7 * m + n, outliers=True)
-    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+def test_gemv_few_tokens_every_output(gpu, m, n, k, out_dtype, fmt):
+    f = FMTS[fmt]
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=7 * m + n, outliers=True, binary=f == BIT1)
+    packed = tl.pack(dev(inp.codes, gpu), f)
     x_rot16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
-    y = host(tl.gemv(packed, dev(inp.scales, gpu), SLOT2, dev(x_rot16, gpu),
+    y = host(tl.gemv(packed, dev(inp.scales, gpu), f, dev(x_rot16, gpu),
                      out_dtype=out_dtype)).astype(np.float64)
     want16 = oracle.matvec(inp.codes, inp.scales, x_rot16)
     # binary16 outputs: the fp32 sum rounded once more (half an ulp, 2^-11)
@@ -54,15 +60,18 @@ def test_gemv_few_tokens_every_output(gpu, m, n, k, out_dtype):
     assert oracle.rel_l2(y, oracle.linear(inp.x, inp.signs, inp.codes, inp.scales)) < 2e-3
 
 
-def test_gemv_few_tokens_row_chunks(gpu):
-    """gate|up concatenated (N = 34816, K = 5120) at M = 8: a
-    workgroup's 136 rows take two row chunks of partial sums; sampled rows in
-    every 64-row tile, all tokens."""
-    k, n, m = 5120, 34816, 8
-    inp = synth.linear_inputs(n, k, m, cfg=3, linear=11, outliers=True)
-    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+@pytest.mark.parametrize("m", [8, 16])
+@pytest.mark.parametrize("fmt", sorted(FMTS))
+def test_gemv_few_tokens_row_chunks(gpu, fmt, m):
+    """gate|up concatenated (N = 34816, K = 5120) at M = 8 and 16: a
+    workgroup's 136 rows (272 with two token groups) take several row chunks
+    of partial sums; sampled rows in every 64-row tile, all tokens."""
+    f = FMTS[fmt]
+    k, n = 5120, 34816
+    inp = synth.linear_inputs(n, k, m, cfg=3, linear=11, outliers=True, binary=f == BIT1)
+    packed = tl.pack(dev(inp.codes, gpu), f)
     x_rot16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
-    y = host(tl.gemv(packed, dev(inp.scales, gpu), SLOT2, dev(x_rot16, gpu))).astype(np.float64)
+    y = host(tl.gemv(packed, dev(inp.scales, gpu), f, dev(x_rot16, gpu))).astype(np.float64)
     rng = np.random.default_rng(5)
     rows = np.unique(np.concatenate([np.arange(0, n, 64), np.arange(63, n, 64),
                                      rng.integers(0, n, size=400)]))

@@ -14,7 +14,10 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt, c
             if (gemv_mt_slot2_fits(m, n, k))
                 return launch_gemv_mt_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
             return launch_gemv_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
-        case 2: return launch_gemv_bit1(packed, scales, x, m, n, k, y, y_f16, stream);
+        case 2:
+            if (gemv_mt_bit1_fits(m, n, k))
+                return launch_gemv_mt_bit1(packed, scales, x, m, n, k, y, y_f16, stream);
+            return launch_gemv_bit1(packed, scales, x, m, n, k, y, y_f16, stream);
         default: return hipErrorInvalidValue;
     }
 }

@@ -39,6 +39,13 @@
 // of their weights finds them in that XCD's L2 cache; every workgroup then
 // owns twice the rows it would with one group.
 //
+// The 1-bit packing (codes -1 and +1, bit b = (code + 1) / 2; page "How Prism
+// ML Squeezed a 27B Model Into 3.9 GB", list "Two formats ship today") runs
+// the same kernel (B1): a lane loads the 8 bytes that hold the same 64
+// weights, and each 16 bits of them are spread into the 2-bit-slot word of
+// those weights (bit i to bit 2i + 1: digit 2b, which is code + 1 as for
+// 2-bit slots); everything after that is shared.
+//
 // Work split and memory pipeline as at M = 1: one 1024-thread workgroup per CU
 // owns a contiguous slice of rows; a wave takes a contiguous run of pair units
 // in pair-major order (its activations change only when the chunk pair does);
@@ -58,6 +65,8 @@ namespace {
 
 using namespace m1;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kUnitRows = 8;                 // rows of a unit (columns of a slot)
 constexpr uint32_t kOnes = 0x55555555u;      // 16 digits 1 (codes 0)
 constexpr int kTokPad = 16;                  // bytes between token images (LDS bank spread)
@@ -71,7 +80,17 @@ constexpr int rounds() { return MT == 2 ? 3 : 2; }
 __host__ __device__ constexpr int tok_stride(int nb) { return nb * kImgBlock + kTokPad; }
 __host__ __device__ constexpr int rec_tok_bytes(int nb) { return nb * 4 * kRecBytes; }
 
-template <int FL, int MT>
+// 16 bits of 1-bit codes (bits 16h .. 16h + 15 of w) as the 2-bit-slot word of
+// the same 16 weights: bit i moves to bit 2i + 1 (digit 2b)
+__device__ __forceinline__ uint32_t spread_bits(uint32_t w, int h) {
+    uint32_t v = __builtin_amdgcn_perm(0u, w, h ? 0x0C030C02u : 0x0C010C00u);   // byte per 16 bits
+    v = (v | (v << 4)) & 0x0F0F0F0Fu;
+    v = (v | (v << 2)) & 0x33333333u;
+    v = (v | (v << 1)) & 0x55555555u;
+    return v << 1;
+}
+
+template <int FL, int MT, bool B1>
 __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int m, int64_t n,
     int64_t k, int sets, int tgroups, int row_base, int row_rem, int rows_per_chunk,
@@ -113,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
     const int64_t y_tok0 = int64_t(grp) * MT;   // first output row of the group
     const int64_t r0 = int64_t(bid) * row_base + min(bid, row_rem);
     const int rows = row_base + (bid < row_rem ? 1 : 0);
-    const int64_t row_bytes = k / 4;
+    const int64_t row_bytes = B1 ? k / 8 : k / 4;
     const int64_t groups = k / kGroup;
     const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(packed + r0 * row_bytes), 0, int(rows * row_bytes), kRsrcWord3);
@@ -135,14 +154,23 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
         end = (wave + 1) * units / kWaves;
         flights = ((units + kWaves - 1) / kWaves + FL - 1) / FL;   // workgroup-uniform
     };
-    uint4 wv[FL];
+    // a lane's weights of a step: 16 bytes of 2-bit slots or 8 bytes of bits
+    using WReg = std::conditional_t<B1, u32x2, uint4>;
+    WReg wv[FL];
     uint32_t sv[FL];
+    auto load_w = [&](uint32_t wo) -> WReg {
+        if constexpr (B1)
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, wo, 0, 0));
+        else
+            return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
+    };
     // offsets of step `u` (a unit index) for this lane; out-of-range -> kOob
     auto offsets = [&](int u, int pp, int g, uint32_t& wo, uint32_t& so) {
         const int r = kUnitRows * g + ip;
         const int c = 2 * pp + s;
         const bool ok = u < end && r < rc;
-        wo = ok ? uint32_t((rc0 + r) * row_bytes + 64 * c + 16 * q) : kOob;
+        const int lane_off = B1 ? 32 * c + 8 * q : 64 * c + 16 * q;
+        wo = ok ? uint32_t((rc0 + r) * row_bytes + lane_off) : kOob;
         so = ok ? uint32_t(((rc0 + r) * groups + 2 * c) * 2) : kOob;
     };
     auto issue = [&](int f, auto t_lo, auto t_hi) {
@@ -153,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
             if (t >= decltype(t_lo)::value && t < decltype(t_hi)::value) {
                 uint32_t wo, so;
                 offsets(f0 + t, c, g, wo, so);
-                wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
+                wv[t] = load_w(wo);
                 sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, 0, 0);
             }
             if (++g == G) {
@@ -222,8 +250,14 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
                 }
                 cur_c = c;
             }
-            const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
-            const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
+            uint4 w4;
+            if constexpr (B1)
+                w4 = uint4{spread_bits(wv[t][0], 0), spread_bits(wv[t][0], 1),
+                           spread_bits(wv[t][1], 0), spread_bits(wv[t][1], 1)};
+            else
+                w4 = wv[t];
+            const auto p01 = __builtin_amdgcn_permlane32_swap(w4.x, w4.y, false, false);
+            const auto p23 = __builtin_amdgcn_permlane32_swap(w4.z, w4.w, false, false);
             float4v dx = float4v{0.0f, 0.0f, 0.0f, 0.0f}, dy = dx;
             dx = mac_eword(p01[0], a[0], a[1], dx);
             dy = mac_eword(p01[1], a[2], a[3], dy);
@@ -246,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(
             if constexpr (RING) {
                 uint32_t wo, so;
                 offsets(g0 + t, c2, gg2, wo, so);
-                wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
+                wv[t] = load_w(wo);
                 sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
                 if (++gg2 == G) {
@@ -404,60 +438,78 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
     return p;
 }
 
-template <int FL, int MT>
+template <int FL, int MT, bool B1>
 hipError_t launch_fl(const MtPlan& p, const uint8_t* packed, const uint16_t* scales,
                      const uint16_t* x, int m, int64_t n, int64_t k, void* y, int y_f16,
                      hipStream_t stream) {
     const int base = int(n / p.sets), rem = int(n % p.sets);
     const hipError_t e =
-        allow_lds(reinterpret_cast<const void*>(gemv_mt_slot2_kernel<FL, MT>), int(kLdsLimit));
+        allow_lds(reinterpret_cast<const void*>(gemv_mt_slot2_kernel<FL, MT, B1>), int(kLdsLimit));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemv_mt_slot2_kernel<FL, MT>), dim3(p.grid), dim3(kThreads), p.lds, stream,
-                       packed, scales, x, m, n, k, p.sets, p.groups, base, rem, p.rpc, y, y_f16);
+    hipLaunchKernelGGL((gemv_mt_slot2_kernel<FL, MT, B1>), dim3(p.grid), dim3(kThreads), p.lds,
+                       stream, packed, scales, x, m, n, k, p.sets, p.groups, base, rem, p.rpc, y,
+                       y_f16);
     return hipGetLastError();
 }
 
 // every token: one or two groups of at most MT tokens
-template <int MT>
+template <int MT, bool B1>
 hipError_t launch_pass(const MtPlan& p, const uint8_t* packed, const uint16_t* scales,
                        const uint16_t* x, int m, int64_t n, int64_t k, void* y, int y_f16,
                        hipStream_t stream) {
     // up to 7 steps a slot: one flight; up to 4 flights of kRingMaxFLMt: a
     // ring; beyond, flights of 7 (8 does not fit the registers)
     if (p.steps > 7 && p.steps <= kRingMaxFLMt * (kRingFlightsMt + 1))
-        return launch_fl<kRingMaxFLMt, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        return launch_fl<kRingMaxFLMt, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
     switch (p.steps) {
-        case 1: return launch_fl<1, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        case 2: return launch_fl<2, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        case 3: return launch_fl<3, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        case 4: return launch_fl<4, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        case 5: return launch_fl<5, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        case 6: return launch_fl<6, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
-        default: return launch_fl<7, MT>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 1: return launch_fl<1, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 2: return launch_fl<2, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 3: return launch_fl<3, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 4: return launch_fl<4, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 5: return launch_fl<5, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        case 6: return launch_fl<6, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
+        default: return launch_fl<7, MT, B1>(p, packed, scales, x, m, n, k, y, y_f16, stream);
     }
 }
 
-}  // namespace
-
-bool gemv_mt_slot2_fits(int64_t m, int64_t n, int64_t k) {
+// bytes per weight row: 2-bit slots or 1-bit codes
+bool mt_fits(int64_t m, int64_t n, int64_t k, int64_t row_bytes) {
     if (m < 2 || m > 16 || k < kBlock || k % kBlock != 0) return false;
     const MtPlan p = mt_plan(m, n, k);
     if (p.mt == 0 || p.rpc < 1 || p.lds > kLdsLimit) return false;
     // at most two token groups; 32-bit buffer offsets within a workgroup's slice
     const int64_t rows = (n + p.sets - 1) / p.sets;
-    return p.groups <= 2 && rows * (k / 4) < (int64_t(1) << 31);
+    return p.groups <= 2 && rows * row_bytes < (int64_t(1) << 31);
 }
+
+template <bool B1>
+hipError_t launch_mt(const uint8_t* packed, const uint16_t* scales, const uint16_t* x, int64_t m,
+                     int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    if (!mt_fits(m, n, k, B1 ? k / 8 : k / 4)) return hipErrorInvalidValue;
+    const MtPlan p = mt_plan(m, n, k);
+    switch (p.mt) {
+        case 2: return launch_pass<2, B1>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
+        case 4: return launch_pass<4, B1>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
+        default: return launch_pass<8, B1>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
+    }
+}
+
+}  // namespace
+
+bool gemv_mt_slot2_fits(int64_t m, int64_t n, int64_t k) { return mt_fits(m, n, k, k / 4); }
 
 hipError_t launch_gemv_mt_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                 int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                                 hipStream_t stream) {
-    if (!gemv_mt_slot2_fits(m, n, k)) return hipErrorInvalidValue;
-    const MtPlan p = mt_plan(m, n, k);
-    switch (p.mt) {
-        case 2: return launch_pass<2>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
-        case 4: return launch_pass<4>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
-        default: return launch_pass<8>(p, packed, scales, x, int(m), n, k, y, y_f16, stream);
-    }
+    return launch_mt<false>(packed, scales, x, m, n, k, y, y_f16, stream);
+}
+
+bool gemv_mt_bit1_fits(int64_t m, int64_t n, int64_t k) { return mt_fits(m, n, k, k / 8); }
+
+hipError_t launch_gemv_mt_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                               int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                               hipStream_t stream) {
+    return launch_mt<true>(packed, scales, x, m, n, k, y, y_f16, stream);
 }
 
 }  // namespace tl

@@ -49,6 +49,12 @@ bool gemv_mt_slot2_fits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_gemv_mt_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                 int64_t m, int64_t n, int64_t k, void* y, int y_f16,
                                 hipStream_t stream);
+// the same kernel for the 1-bit packing (each 16 bits of codes spread into a
+// 2-bit-slot word); usable when gemv_mt_bit1_fits(m, n, k)
+bool gemv_mt_bit1_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv_mt_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                               int64_t m, int64_t n, int64_t k, void* y, int y_f16,
+                               hipStream_t stream);
 // Dense trits at M = 1 with the rotation fused in front (x unrotated; x_rot
 // receives the rotated activations); usable when linear_m1_trit5_fits
 bool linear_m1_trit5_fits(int64_t m, int64_t n, int64_t k);
