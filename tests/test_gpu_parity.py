@@ -353,6 +353,30 @@ def test_linear_fused_plan_edges(gpu, fmt, n, k, out_dtype):
     assert oracle.rel_l2(y.astype(np.float64), want) < 2e-3
 
 
+@pytest.mark.parametrize("n,k", [(35071, 5120), (31234, 17408), (1031, 3072)])
+def test_m1_row_layouts(gpu, n, k):
+    """The 2-bit M = 1 kernels where a workgroup's rows are not a multiple of
+    the four rows a wave takes per step (137 and 136 rows: the last unit of
+    each block overlaps the one before), where they take two row chunks
+    (122 or 123 rows at K = 17408: the second chunk has fewer than four rows),
+    and a small ragged case.  Sampled rows in every 64-row tile against the
+    oracle on the binary16 x_rot the call wrote; tl_linear equals tl_gemv on
+    that x_rot bit for bit."""
+    fmt = tl.FMT_SLOT2
+    inp = synth.linear_inputs(n, k, 1, cfg=3, linear=n + 3, outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), fmt)
+    scales = dev(inp.scales, gpu)
+    x_rot = torch.empty((1, k), dtype=torch.float16, device=gpu)
+    y = host(tl.linear(packed, scales, fmt, dev(inp.x, gpu), dev(inp.signs, gpu), x_rot=x_rot))
+    y2 = host(tl.gemv(packed, scales, fmt, x_rot))
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([np.arange(0, n, 64), np.arange(63, n, 64), [n - 1],
+                                     rng.integers(0, n, size=256)]))
+    want = oracle.matvec(inp.codes[rows], inp.scales[rows], host(x_rot))
+    assert oracle.rel_l2(y[:, rows].astype(np.float64), want) < 1e-5
+
+
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
 @pytest.mark.parametrize("shape", ["gate", "down", "k"])
 def test_linear_full_size_sampled_rows(gpu, fmt, shape):

@@ -36,8 +36,10 @@
 // reads bytes [16u, 16u + 16), so a column reads 64 contiguous bytes = two
 // groups; lanes l / 16 < 2 hold the first group, the others the second, and
 // v_permlane32_swap exchanges words so that each MFMA sees one group only.
-// Slots take contiguous runs of segments, block-major, so a slot's
-// activations change rarely.  The first two steps' weight loads are in
+// The four slots of a wave take four consecutive rows of the same block per
+// step (a unit); a wave takes a contiguous run of units, block-major, so its
+// activations change rarely, and every address of a step is a wave-uniform
+// offset plus a per-lane constant.  The first two steps' weight loads are in
 // flight while the per-lane activation images are built once per workgroup in
 // LDS; the rest of a slot's loads follow, all before its first wait on
 // weights.  Per-segment sums go to LDS and are added in a fixed order (bitwise
@@ -81,7 +83,6 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     const int slot_in_wave = col >> 2;
     const int ip = lane & 3;                 // column within the slot
     const int u = 4 * ip + q;                // lane rank within the segment
-    const int slot = 4 * wave + slot_in_wave;
     const bool diag = q == slot_in_wave;     // this lane holds D[col][col]
 
     // rows [r0, r0 + rows): row_base rows each, one more for the first row_rem
@@ -95,71 +96,100 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     const __amdgpu_buffer_rsrc_t ssrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(scales + r0 * groups), 0, int(rows * groups * 2), kRsrcWord3);
 
-    // Per chunk of rows: the slot's segment range [beg, end) (block-major),
-    // in flights of FL steps.
-    int rc0 = 0, rc = 0, beg = 0, end = 0, flights = 0;
+    // Per chunk of rows, work in units of four rows x one 1024-block (one row
+    // per slot of a wave, the same block for the wave's four slots),
+    // block-major; wave w takes units [vb, ve) in flights of FL steps.  The
+    // unit, its block and its first row are wave-uniform, so every address
+    // of a step is a scalar offset plus a per-lane constant (no per-step
+    // vector arithmetic).  A block's last unit starts at row rc - 4 (its rows
+    // overlap the unit before: those partial sums are computed twice and
+    // written twice with the same bits); with fewer than four rows the slots
+    // past the last row repeat it.  Steps past a wave's last unit repeat that
+    // unit the same way.
+    int rc0 = 0, rc = 0, U = 1, vb = 0, ve = 0, flights = 0;
+    uint32_t w_lane = 0, s_lane = 0;
+    int red_lane = 0;
+    // a step's unit: index v, block b, unit j of the block (all wave-uniform)
+    struct Cur {
+        int v, b, j;
+    };
+    Cur first{0, 0, 0};  // the wave's first unit of the chunk
+    Cur last{0, 0, 0};   // the unit that steps past the wave's last one repeat
+    auto cur_at = [&](int v) {
+        const int b = v / U;
+        return Cur{v, b, v - b * U};
+    };
+    auto cur_next = [&](Cur c) {
+        ++c.v;
+        if (++c.j == U) {
+            c.j = 0;
+            ++c.b;
+        }
+        return c;
+    };
+    auto advance = [&](Cur c) {
+#pragma unroll
+        for (int t = 0; t < FL; ++t) c = cur_next(c);
+        return c;
+    };
+    auto eff = [&](const Cur& c) { return c.v < ve ? c : last; };
     auto set_chunk = [&](int c0) {
         rc0 = c0;
         rc = min(rows_per_chunk, rows - c0);
-        const int segs = rc * nb;
-        beg = slot * segs / kSlots;
-        end = (slot + 1) * segs / kSlots;
-        flights = ((segs + kSlots - 1) / kSlots + FL - 1) / FL;   // workgroup-uniform
+        U = (rc + 3) / 4;
+        const int units = U * nb;
+        vb = wave * units / kWaves;
+        ve = (wave + 1) * units / kWaves;
+        last = cur_at(ve > vb ? ve - 1 : units - 1);
+        first = cur_at(vb);
+        flights = ((units + kWaves - 1) / kWaves + FL - 1) / FL;   // workgroup-uniform
+        const int s_eff = min(slot_in_wave, rc - 1);
+        w_lane = uint32_t(s_eff * int(row_bytes) + 16 * u);
+        s_lane = uint32_t((s_eff * int(groups) + 2 * ip) * 2);
+        red_lane = s_eff * nb * 4 + ip;
     };
+    auto row0 = [&](const Cur& c) { return rc < 4 ? 0 : min(4 * c.j, rc - 4); };
     uint4 wv[FL];
     uint32_t sv[FL];
-    // every weight and scale load of steps [t_lo, t_hi) of a flight; steps past
-    // the slot's end read nothing (out-of-range offsets return zeros)
-    auto issue = [&](int f, auto t_lo, auto t_hi) {
-        const int f0 = beg + f * FL;
-        int b = f0 / rc, r = f0 - (f0 / rc) * rc;
+    auto load_step = [&](int t, const Cur& c) {
+        const Cur e = eff(c);
+        const int r = rc0 + row0(e);
+        wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              wsrc, w_lane, uint32_t(r * int(row_bytes) + 256 * e.b), 0));
+        sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, s_lane,
+                                                     uint32_t((r * int(groups) + 8 * e.b) * 2), 0);
+    };
+    // every weight and scale load of steps [t_lo, t_hi) of the flight starting at c
+    auto issue = [&](Cur c, auto t_lo, auto t_hi) {
 #pragma unroll
         for (int t = 0; t < FL; ++t) {
-            const bool ok = f0 + t < end;
-            if (t < decltype(t_lo)::value || t >= decltype(t_hi)::value) {
-                if (++r == rc) {
-                    r = 0;
-                    ++b;
-                }
-                continue;
-            }
-            const uint32_t wo = ok ? uint32_t((rc0 + r) * row_bytes + 256 * b + 16 * u) : kOob;
-            const uint32_t so = ok ? uint32_t(((rc0 + r) * groups + 8 * b + 2 * ip) * 2) : kOob;
-            wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
-            sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, 0, 0);
-            if (++r == rc) {
-                r = 0;
-                ++b;
-            }
+            if (t >= decltype(t_lo)::value && t < decltype(t_hi)::value) load_step(t, c);
+            c = cur_next(c);
         }
     };
     int cur_b = -1;
     half8 a[8];
     float rf = 0.0f, rx = 0.0f, ry = 0.0f;
-    // Flight f.  With RING, as soon as step t is consumed its registers
-    // receive step t of flight f + 1 (the loads stay in step order, so the
-    // compiler waits for exactly the step it consumes): the weight stream
-    // does not pause between flights.
-    auto run = [&](int f, auto ring_c) {
+    // The flight starting at c.  With RING, as soon as step t is consumed its
+    // registers receive step t of the next flight (starting at c2; the loads
+    // stay in step order, so the compiler waits for exactly the step it
+    // consumes): the weight stream does not pause between flights.
+    auto run = [&](Cur c, Cur c2, auto ring_c) {
         constexpr bool RING = decltype(ring_c)::value;
-        const int f0 = beg + f * FL;
-        int b = f0 / rc, r = f0 - (f0 / rc) * rc;
-        const int g0 = f0 + FL;
-        int b2 = g0 / rc, r2 = g0 - (g0 / rc) * rc;
 #pragma unroll
         for (int t = 0; t < FL; ++t) {
-            const bool ok = f0 + t < end;
-            if (ok && b != cur_b) {   // slot-uniform; rare (slots run block-major)
-                const uint8_t* src = img + b * kImgBlock + u * kImgLane;
+            const Cur e = eff(c);
+            if (e.b != cur_b) {   // wave-uniform; rare (units run block-major)
+                const uint8_t* src = img + e.b * kImgBlock + u * kImgLane;
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    a[j] = __builtin_bit_cast(
-                        half8, *reinterpret_cast<const lds_u32x4*>(lds_addr(src + 16 * j)));
-                const float4 rv = *reinterpret_cast<const float4*>(rec + (b * 4 + ip) * kRecBytes);
+                for (int jj = 0; jj < 8; ++jj)
+                    a[jj] = __builtin_bit_cast(
+                        half8, *reinterpret_cast<const lds_u32x4*>(lds_addr(src + 16 * jj)));
+                const float4 rv = *reinterpret_cast<const float4*>(rec + (e.b * 4 + ip) * kRecBytes);
                 rf = rv.x;
                 rx = rv.y;
                 ry = rv.z;
-                cur_b = b;
+                cur_b = e.b;
             }
             const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
             const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
@@ -172,22 +202,12 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
             const float part = (h2f(sv[t] & 0xFFFFu) * (pick(dx, ip) + rx) +
                                 h2f(sv[t] >> 16) * (pick(dy, ip) + ry)) *
                                rf;
-            if (diag && ok) red[(r * nb + b) * 4 + ip] = part;
-            if (++r == rc) {
-                r = 0;
-                ++b;
-            }
+            if (diag) red[red_lane + (row0(e) * nb + e.b) * 4] = part;
+            c = cur_next(c);
             if constexpr (RING) {
-                const bool ok2 = g0 + t < end;
-                const uint32_t wo = ok2 ? uint32_t((rc0 + r2) * row_bytes + 256 * b2 + 16 * u) : kOob;
-                const uint32_t so = ok2 ? uint32_t(((rc0 + r2) * groups + 8 * b2 + 2 * ip) * 2) : kOob;
-                wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, wo, 0, 0));
-                sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, so, 0, 0);
+                load_step(t, c2);
                 __builtin_amdgcn_sched_barrier(0);
-                if (++r2 == rc) {
-                    r2 = 0;
-                    ++b2;
-                }
+                c2 = cur_next(c2);
             }
         }
     };
@@ -238,7 +258,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         uint4 sr[2];
         rot::load(x, signs, nb, tid, xraw, sr);
         set_chunk(0);
-        issue(0, Zero{}, Head{});
+        issue(first, Zero{}, Head{});
         __builtin_amdgcn_sched_barrier(0);   // the rotation stays below those weight loads
         rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
                  kBlock);   // nb <= 32 half-waves
@@ -251,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     } else {
         load_x(x, nb, tid, xraw);
         set_chunk(0);
-        issue(0, Zero{}, Head{});
+        issue(first, Zero{}, Head{});
         __builtin_amdgcn_sched_barrier(0);   // the image build stays below those weight loads
         if (wave * 64 < nb * 32) build_pass(xraw, nb, tid, img, rec);   // nb * 32 <= kThreads
     }
@@ -263,25 +283,34 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         // in flight when it starts (a real wait instruction, which the
         // compiler's wait placement takes into account)
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vector memory count 0
-        issue(0, Head{}, All{});
+        issue(first, Head{}, All{});
+        Cur c = first;
 #pragma unroll
         for (int f = 0; f < kRingFlights; ++f)
-            if (f + 1 < flights) run(f, Ring{});
-        run(flights - 1, Plain{});
+            if (f + 1 < flights) {
+                const Cur n = advance(c);
+                run(c, n, Ring{});
+                c = n;
+            }
+        run(c, c, Plain{});
     } else {
-        issue(0, Head{}, All{});
-        run(0, Plain{});
+        issue(first, Head{}, All{});
+        run(first, first, Plain{});
+        Cur c = first;
         for (int f = 1; f < flights; ++f) {
-            issue(f, Zero{}, All{});
-            run(f, Plain{});
+            c = advance(c);
+            issue(c, Zero{}, All{});
+            run(c, c, Plain{});
         }
     }
     finish_chunk();
     for (int c0 = rows_per_chunk; c0 < rows; c0 += rows_per_chunk) {
         set_chunk(c0);
+        Cur c = first;
         for (int f = 0; f < flights; ++f) {
-            issue(f, Zero{}, All{});
-            run(f, Plain{});
+            issue(c, Zero{}, All{});
+            run(c, c, Plain{});
+            c = advance(c);
         }
         finish_chunk();
     }
@@ -317,7 +346,7 @@ M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     M1Plan p;
     p.grid = unsigned(grid);
     p.rpc = int(rpc);
-    p.steps = int((rpc * nb + kSlots - 1) / kSlots);
+    p.steps = int(((rpc + 3) / 4 * nb + kWaves - 1) / kWaves);   // units of 4 rows per wave
     const size_t tail = size_t(nb) * kImgBlock + size_t(nb) * 4 * kRecBytes + size_t(rpc * nb) * 16;
     const size_t scratch = size_t(nb) * rot::kScratchBytes;
     p.lds = rot ? size_t(nb) * 2048 + (tail > scratch ? tail : scratch) : tail;
