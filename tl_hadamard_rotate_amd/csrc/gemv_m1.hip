@@ -115,8 +115,15 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     };
     Cur first{0, 0, 0};  // the wave's first unit of the chunk
     Cur last{0, 0, 0};   // the unit that steps past the wave's last one repeat
+    // v / U by a float reciprocal and one correction (v < 2^20): a scalar
+    // integer division is a long sequence of scalar instructions, which the
+    // four SIMDs of a CU share
     auto cur_at = [&](int v) {
-        const int b = v / U;
+        int b = int(float(v) * __builtin_amdgcn_rcpf(float(U)));
+        if ((b + 1) * U <= v)
+            ++b;
+        else if (b * U > v)
+            --b;
         return Cur{v, b, v - b * U};
     };
     auto cur_next = [&](Cur c) {
