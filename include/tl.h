@@ -28,6 +28,15 @@
  *   - The library keeps no state between calls apart from that per-thread
  *     error text and, per device, the compute-unit count and the kernels' LDS
  *     limits, looked up on first use; calls from several threads are safe.
+ *   - Debug checks: with the environment variable TL_DEBUG=1, tl_unpack,
+ *     tl_gemv, tl_gemm, tl_gemm_bf16 and tl_linear first count the packed
+ *     bytes that are not valid encodings (see Formats) on the device, wait
+ *     for the count on `stream`, and return TL_ERR_DATA (count in
+ *     tl_last_error()) without launching anything else when there is any.
+ *     This mode synchronises, allocates one small device buffer per GPU on
+ *     first use and serialises the checks of concurrent calls; it is skipped
+ *     while `stream` is being captured, and tl_gemm_noalloc and
+ *     tl_linear_chain never check.
  *
  * Formats (bit-exact; defined here, since the pages give no byte layout)
  *   digit d = code + 1, in {0, 1, 2}.
@@ -75,7 +84,8 @@ typedef enum {
     TL_ERR_ALIAS = 5,    /* an output overlaps an input it must not overlap    */
     TL_ERR_LAUNCH = 6,   /* the HIP launch failed; see tl_last_error()         */
     TL_ERR_DTYPE = 7,    /* unknown output dtype                               */
-    TL_ERR_WORKSPACE = 8 /* workspace missing or smaller than the call needs   */
+    TL_ERR_WORKSPACE = 8, /* workspace missing or smaller than the call needs  */
+    TL_ERR_DATA = 9      /* invalid packed bytes found (only with TL_DEBUG=1)  */
 } tl_status;
 
 enum { TL_FMT_TRIT5 = 0, TL_FMT_SLOT2 = 1, TL_FMT_BIT1 = 2 };

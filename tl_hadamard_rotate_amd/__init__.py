@@ -27,7 +27,7 @@ GROUP = 128
 
 _STATUS = {0: "TL_OK", 1: "TL_ERR_NULL", 2: "TL_ERR_SHAPE", 3: "TL_ERR_FORMAT",
            4: "TL_ERR_ALIGN", 5: "TL_ERR_ALIAS", 6: "TL_ERR_LAUNCH", 7: "TL_ERR_DTYPE",
-           8: "TL_ERR_WORKSPACE"}
+           8: "TL_ERR_WORKSPACE", 9: "TL_ERR_DATA"}
 
 _lib = None
 
@@ -82,7 +82,7 @@ def lib() -> ctypes.CDLL:
 
 def _check(call: str, status: int) -> None:
     if status != 0:
-        detail = lib().tl_last_error().decode() if status == 6 else ""
+        detail = lib().tl_last_error().decode() if status in (6, 9) else ""
         raise TLError(call, status, detail)
 
 

@@ -220,7 +220,36 @@ unsigned grid_for(int64_t total) {
     return unsigned(blocks);
 }
 
+// One thread per packed byte: counts the bytes that are not valid encodings
+// (a 2-bit slot holding 3; a dense-trit byte above 242, or a group's last
+// byte whose two pad digits are not 1, i.e. outside 108..134).
+__global__ __launch_bounds__(kThreads) void count_invalid_kernel(
+    const uint8_t* __restrict__ packed, int64_t total, int64_t group_bytes, int fmt,
+    int32_t* __restrict__ count) {
+    uint32_t bad = 0;
+    for (int64_t idx = int64_t(blockIdx.x) * kThreads + threadIdx.x; idx < total;
+         idx += int64_t(gridDim.x) * kThreads) {
+        const uint32_t v = packed[idx];
+        if (fmt == 0) {
+            const bool last = idx % group_bytes == group_bytes - 1;
+            bad += last ? (v < 108u || v > 134u) : (v > 242u);
+        } else {
+            bad += ((v & 0x55u) & ((v >> 1) & 0x55u)) != 0u;
+        }
+    }
+    if (bad) atomicAdd(count, int32_t(bad));
+}
+
 }  // namespace
+
+hipError_t launch_count_invalid(const uint8_t* packed, int64_t n, int64_t k, int fmt,
+                                int32_t* count, hipStream_t stream) {
+    if (fmt == 2) return hipSuccess;   // every byte of the 1-bit format is valid
+    const int64_t total = fmt == 0 ? n * (k / kGroup) * kTrit5GroupBytes : n * k / 4;
+    hipLaunchKernelGGL(count_invalid_kernel, dim3(grid_for(total)), dim3(kThreads), 0, stream,
+                       packed, total, int64_t(kTrit5GroupBytes), fmt, count);
+    return hipGetLastError();
+}
 
 hipError_t launch_pack(const int8_t* codes, int64_t n, int64_t k, int fmt, uint8_t* packed,
                        int32_t* bad_count, hipStream_t stream) {

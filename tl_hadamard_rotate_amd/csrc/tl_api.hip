@@ -3,7 +3,9 @@
 // leaves every output untouched.
 #include <stdint.h>
 
+#include <cstdlib>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 #include <utility>
 
@@ -77,6 +79,46 @@ tl_status check_workspace(int64_t need, const void* ws, int64_t ws_bytes,
     return TL_OK;
 }
 
+// TL_DEBUG=1: count the packed bytes that are not valid encodings before a
+// call that decodes them; a device int per GPU holds the count
+bool debug_on() {
+    const char* e = std::getenv("TL_DEBUG");
+    return e && e[0] == '1' && e[1] == '\0';
+}
+
+tl_status debug_check(const uint8_t* packed, int64_t n, int64_t k, int32_t fmt, hipStream_t stream) {
+    if (!debug_on() || fmt == TL_FMT_BIT1) return TL_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return launched(e);
+    if (cs != hipStreamCaptureStatusNone) return TL_OK;   // no waiting inside a capture
+    static std::mutex mu;
+    static int32_t* counters[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return launched(e);
+    if (dev < 0 || dev >= 64) return launched(hipErrorInvalidDevice);
+    if (!counters[dev]) {
+        void* p = nullptr;
+        e = hipMalloc(&p, 256);
+        if (e != hipSuccess) return launched(e);
+        counters[dev] = static_cast<int32_t*>(p);
+    }
+    int32_t bad = 0;
+    e = hipMemsetAsync(counters[dev], 0, sizeof(int32_t), stream);
+    if (e == hipSuccess) e = tl::launch_count_invalid(packed, n, k, fmt, counters[dev], stream);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&bad, counters[dev], sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return launched(e);
+    if (bad != 0) {
+        g_last_error = std::to_string(bad) + " packed bytes are not valid encodings";
+        return TL_ERR_DATA;
+    }
+    return TL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -108,6 +150,8 @@ tl_status tl_unpack(const uint8_t* packed, int64_t N, int64_t K, int32_t fmt, in
     if (!known_fmt(fmt)) return TL_ERR_FORMAT;
     if (!aligned16(codes) || !aligned16(packed)) return TL_ERR_ALIGN;
     if (overlap(packed, N * row_bytes(K, fmt), codes, N * K)) return TL_ERR_ALIAS;
+    const tl_status st = debug_check(packed, N, K, fmt, stream);
+    if (st != TL_OK) return st;
     return launched(tl::launch_unpack(packed, N, K, fmt, codes, stream));
 }
 
@@ -126,7 +170,9 @@ tl_status tl_hadamard_rotate(const uint16_t* x, const int8_t* signs, int64_t M, 
 
 tl_status tl_gemv(const uint8_t* packed, const uint16_t* scales, int32_t fmt, const uint16_t* x_rot,
                   int64_t M, int64_t N, int64_t K, void* y, int32_t y_dtype, hipStream_t stream) {
-    const tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    tl_status st = check_layer(packed, scales, fmt, x_rot, M, N, K, y, y_dtype);
+    if (st != TL_OK) return st;
+    st = debug_check(packed, N, K, fmt, stream);
     if (st != TL_OK) return st;
     return launched(
         tl::launch_gemv(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16, stream));
@@ -163,6 +209,8 @@ tl_status tl_gemm(const uint8_t* packed, const uint16_t* scales, int32_t fmt, co
                          {{packed, N * row_bytes(K, fmt)}, {scales, N * (K / TL_GROUP) * 2},
                           {x_rot, M * K * 2}, {y, M * N * (y_dtype == TL_F32 ? 4 : 2)}});
     if (st != TL_OK) return st;
+    st = debug_check(packed, N, K, fmt, stream);
+    if (st != TL_OK) return st;
     return launched(tl::launch_gemm(packed, scales, fmt, x_rot, M, N, K, y, y_dtype == TL_F16,
                                     workspace, workspace_bytes, stream));
 }
@@ -195,6 +243,8 @@ tl_status tl_gemm_bf16(const uint8_t* packed, const uint16_t* scales, int32_t fm
                          {{packed, N * row_bytes(K, fmt)}, {scales, N * (K / TL_GROUP) * 2},
                           {x_rot, M * K * 2}, {y, M * N * (y_dtype == TL_F32 ? 4 : 2)}});
     if (st != TL_OK) return st;
+    st = debug_check(packed, N, K, fmt, stream);
+    if (st != TL_OK) return st;
     return launched(tl::launch_gemm_bf16(packed, scales, fmt, x_rot, M, N, K, y,
                                          y_dtype == TL_F16, workspace, workspace_bytes, stream));
 }
@@ -222,6 +272,8 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
                               {x, xb}, {signs, K}, {x_rot, xb}, {y, yb}});
         if (st != TL_OK) return st;
     }
+    st = debug_check(packed, N, K, fmt, stream);
+    if (st != TL_OK) return st;
     const int y_f16 = y_dtype == TL_F16;
     if (fmt == TL_FMT_SLOT2 && tl::linear_m1_slot2_fits(M, N, K))
         return launched(
@@ -287,6 +339,7 @@ const char* tl_status_str(tl_status status) {
         case TL_ERR_LAUNCH: return "TL_ERR_LAUNCH";
         case TL_ERR_DTYPE: return "TL_ERR_DTYPE";
         case TL_ERR_WORKSPACE: return "TL_ERR_WORKSPACE";
+        case TL_ERR_DATA: return "TL_ERR_DATA";
     }
     return "TL_ERR_UNKNOWN";
 }

@@ -69,6 +69,10 @@ hipError_t launch_gemv_trit5(const uint8_t* packed, const uint16_t* scales, cons
 hipError_t launch_trit5_to_slot2(const uint8_t* trit5, int64_t n, int64_t k, uint8_t* slot2,
                                  hipStream_t stream);
 // The 1-bit packing rewritten as 2-bit slots (digit 2b), row-major [n][k/4] bytes.
+// count of packed bytes that are not valid encodings of format fmt, added to
+// *count (a device int the caller cleared)
+hipError_t launch_count_invalid(const uint8_t* packed, int64_t n, int64_t k, int fmt,
+                                int32_t* count, hipStream_t stream);
 hipError_t launch_bit1_to_slot2(const uint8_t* bit1, int64_t n, int64_t k, uint8_t* slot2,
                                 hipStream_t stream);
 // Decode GEMV of the 1-bit packing (any m; tokens in launches of at most 16)
