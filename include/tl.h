@@ -17,8 +17,9 @@
  *
  * Conventions shared by every call
  *   - All tensors are dense row-major device buffers owned by the caller; the
- *     library never allocates, frees or retains device memory.  The prefill
- *     products take a caller-owned workspace (tl_gemm_workspace_bytes).
+ *     library never allocates, frees or retains device memory (outside the
+ *     opt-in debug checks below).  The prefill products take a caller-owned
+ *     workspace (tl_gemm_workspace_bytes).
  *   - binary16 data is passed as uint16_t (bit patterns).
  *   - Every call validates its arguments first.  On a validation failure it
  *     returns the status and launches nothing, so outputs are untouched.
