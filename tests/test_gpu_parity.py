@@ -353,15 +353,16 @@ def test_linear_fused_plan_edges(gpu, fmt, n, k, out_dtype):
     assert oracle.rel_l2(y.astype(np.float64), want) < 2e-3
 
 
-@pytest.mark.parametrize("n,k", [(35071, 5120), (31234, 17408), (1031, 3072)])
+@pytest.mark.parametrize("n,k", [(35071, 5120), (31234, 17408), (60000, 4096), (1031, 3072)])
 def test_m1_row_layouts(gpu, n, k):
     """The 2-bit M = 1 kernels where a workgroup's rows are not a multiple of
     the four rows a wave takes per step (137 and 136 rows: the last unit of
-    each block overlaps the one before), where they take two row chunks
-    (122 or 123 rows at K = 17408: the second chunk has fewer than four rows),
-    and a small ragged case.  Sampled rows in every 64-row tile against the
-    oracle on the binary16 x_rot the call wrote; tl_linear equals tl_gemv on
-    that x_rot bit for bit."""
+    each block overlaps the one before), where they take two row chunks (122
+    or 123 rows at K = 17408: the second chunk has fewer than four rows),
+    where a wave's 15 steps run as a ring of three flights (234 or 235 rows
+    at K = 4096), and a small ragged case.  Sampled rows in every
+    64-row tile against the oracle on the binary16 x_rot the call wrote;
+    tl_linear equals tl_gemv on that x_rot bit for bit."""
     fmt = tl.FMT_SLOT2
     inp = synth.linear_inputs(n, k, 1, cfg=3, linear=n + 3, outliers=True)
     packed = tl.pack(dev(inp.codes, gpu), fmt)

@@ -126,12 +126,16 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
             --b;
         return Cur{v, b, v - b * U};
     };
+    // (the block passes through readfirstlane: else the compiler may form its
+    // increment as a vector add with carry, and each load offset made from
+    // it becomes a loop over the lanes' distinct values)
     auto cur_next = [&](Cur c) {
         ++c.v;
         if (++c.j == U) {
             c.j = 0;
             ++c.b;
         }
+        c.b = __builtin_amdgcn_readfirstlane(c.b);
         return c;
     };
     auto advance = [&](Cur c) {
