@@ -772,10 +772,14 @@ def build_mlp_step(torch, tl, synth, dev, copies, fmt=1):
 
 
 def per_launch_times_us(torch, steps, reps, stream):
-    """Average duration of each launch of a step, measured with HIP events
-    recorded on the launch stream between consecutive launches; everything is
-    enqueued behind a GPU sleep, so that the time between two events is the
-    launch's dispatch and execution, not the host's submission."""
+    """Duration of each launch of a step, measured with HIP events recorded on
+    the launch stream between consecutive launches; everything is enqueued
+    behind a GPU sleep, so that the time between two events is the launch's
+    dispatch and execution, not the host's submission.  The median over the
+    `reps` steps (at most 100, so that every launch and event fits in the
+    queue before the sleep ends: a longer run made the host enqueue while the
+    GPU waited, and single rows read tens of microseconds)."""
+    reps = min(reps, 100)
     import statistics
     with torch.cuda.stream(stream):
         torch.cuda.synchronize()
@@ -792,7 +796,7 @@ def per_launch_times_us(torch, steps, reps, stream):
             rows.append(row)
         torch.cuda.synchronize()
     n = len(rows[0]) - 1
-    return [statistics.mean(row[j].elapsed_time(row[j + 1]) for row in rows) * 1e3 for j in range(n)]
+    return [statistics.median(row[j].elapsed_time(row[j + 1]) for row in rows) * 1e3 for j in range(n)]
 
 
 def per_launch_us(torch, graphs, reps, stream):

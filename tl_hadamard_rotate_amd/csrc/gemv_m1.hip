@@ -160,15 +160,22 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         red_lane = s_eff * nb * 4 + ip;
     };
     auto row0 = [&](const Cur& c) { return rc < 4 ? 0 : min(4 * c.j, rc - 4); };
+    // Step t of a flight: its weights and scales in registers, and (scalar)
+    // its block and the offset of its partial sums in red, set when its loads
+    // are issued so that consuming it takes no unit arithmetic.
     uint4 wv[FL];
     uint32_t sv[FL];
+    int sb[FL], sro[FL];
     auto load_step = [&](int t, const Cur& c) {
         const Cur e = eff(c);
-        const int r = rc0 + row0(e);
+        const int r0e = row0(e);
+        const int r = rc0 + r0e;
         wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                               wsrc, w_lane, uint32_t(r * int(row_bytes) + 256 * e.b), 0));
         sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, s_lane,
                                                      uint32_t((r * int(groups) + 8 * e.b) * 2), 0);
+        sb[t] = e.b;
+        sro[t] = (r0e * nb + e.b) * 4;
     };
     // every weight and scale load of steps [t_lo, t_hi) of the flight starting at c
     auto issue = [&](Cur c, auto t_lo, auto t_hi) {
@@ -181,26 +188,26 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     int cur_b = -1;
     half8 a[8];
     float rf = 0.0f, rx = 0.0f, ry = 0.0f;
-    // The flight starting at c.  With RING, as soon as step t is consumed its
-    // registers receive step t of the next flight (starting at c2; the loads
-    // stay in step order, so the compiler waits for exactly the step it
-    // consumes): the weight stream does not pause between flights.
-    auto run = [&](Cur c, Cur c2, auto ring_c) {
+    // The flight whose loads were issued last.  With RING, as soon as step t
+    // is consumed its registers receive step t of the next flight (starting
+    // at c2; the loads stay in step order, so the compiler waits for exactly
+    // the step it consumes): the weight stream does not pause between flights.
+    auto run = [&](Cur c2, auto ring_c) {
         constexpr bool RING = decltype(ring_c)::value;
 #pragma unroll
         for (int t = 0; t < FL; ++t) {
-            const Cur e = eff(c);
-            if (e.b != cur_b) {   // wave-uniform; rare (units run block-major)
-                const uint8_t* src = img + e.b * kImgBlock + u * kImgLane;
+            const int b = sb[t];
+            if (b != cur_b) {   // wave-uniform; rare (units run block-major)
+                const uint8_t* src = img + b * kImgBlock + u * kImgLane;
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj)
                     a[jj] = __builtin_bit_cast(
                         half8, *reinterpret_cast<const lds_u32x4*>(lds_addr(src + 16 * jj)));
-                const float4 rv = *reinterpret_cast<const float4*>(rec + (e.b * 4 + ip) * kRecBytes);
+                const float4 rv = *reinterpret_cast<const float4*>(rec + (b * 4 + ip) * kRecBytes);
                 rf = rv.x;
                 rx = rv.y;
                 ry = rv.z;
-                cur_b = e.b;
+                cur_b = b;
             }
             const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
             const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
@@ -213,8 +220,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
             const float part = (h2f(sv[t] & 0xFFFFu) * (pick(dx, ip) + rx) +
                                 h2f(sv[t] >> 16) * (pick(dy, ip) + ry)) *
                                rf;
-            if (diag) red[red_lane + (row0(e) * nb + e.b) * 4] = part;
-            c = cur_next(c);
+            if (diag) red[red_lane + sro[t]] = part;
             if constexpr (RING) {
                 load_step(t, c2);
                 __builtin_amdgcn_sched_barrier(0);
@@ -300,18 +306,18 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         for (int f = 0; f < kRingFlights; ++f)
             if (f + 1 < flights) {
                 const Cur n = advance(c);
-                run(c, n, Ring{});
+                run(n, Ring{});
                 c = n;
             }
-        run(c, c, Plain{});
+        run(c, Plain{});
     } else {
         issue(first, Head{}, All{});
-        run(first, first, Plain{});
+        run(first, Plain{});
         Cur c = first;
         for (int f = 1; f < flights; ++f) {
             c = advance(c);
             issue(c, Zero{}, All{});
-            run(c, c, Plain{});
+            run(c, Plain{});
         }
     }
     finish_chunk();
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         Cur c = first;
         for (int f = 0; f < flights; ++f) {
             issue(c, Zero{}, All{});
-            run(c, c, Plain{});
+            run(c, Plain{});
             c = advance(c);
         }
         finish_chunk();
