@@ -101,27 +101,6 @@ constexpr int kDeviceScope = 16;
 // s_waitcnt immediate: vector memory count 0, the other counters not waited
 constexpr int kVmcntZero = 0x0F70;
 
-// rot::load with device-scope loads of x
-__device__ __forceinline__ void load_x_coherent(const uint16_t* x, const int8_t* signs, int nb,
-                                                int t, uint4 (&xr)[4], uint4 (&sr)[2]) {
-    const int hw = t >> 5, j = t & 31;
-    const __amdgpu_buffer_rsrc_t xs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(x), 0, nb * 2048, kRsrcWord3);
-    const __amdgpu_buffer_rsrc_t ss =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(signs), 0, nb * 1024, kRsrcWord3);
-    const bool live = hw < nb;
-    const uint32_t xo = uint32_t((1024 * hw + 32 * j) * 2);
-    const uint32_t so = uint32_t(1024 * hw + 32 * j);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              xs, live ? xo + 16 * i : kOob, 0, kDeviceScope));
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-        sr[i] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(ss, live ? so + 16 * i : kOob, 0, 0));
-}
-
 template <int FL, int CROSS, int MAXF>
 __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restrict__ plan, int count,
                                                          uint32_t* sync) {
@@ -317,13 +296,20 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
             }
             if (i > 0 && wave == 0) load_steps(loads_of(st, 0, true), 0, CROSS);
 
-            // rotation of the input into LDS (x_rot written by workgroup 0),
-            // then the activation images
+            // rotation of the input into LDS as tl_linear's kernel does it (x_rot
+            // written by workgroup 0; the input read at device scope), then the
+            // activation images
             {
-                uint4 xraw[4], sr[2];
-                load_x_coherent(op.x, op.signs, nb, tid, xraw, sr);
-                rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
-                         kBlock);   // nb <= 32 half-waves
+                // one block's input in registers at a time: this kernel holds
+                // the next linear's first weight steps through the rotation
+                rotm::half8v hb[2];
+                rotm::h_operand(lane, hb);
+                for (int blk = wave; blk < nb; blk += kWaves) {
+                    rotm::In rin;
+                    rotm::load<kDeviceScope>(op.x, op.signs, nb, blk, lane, rin);
+                    rotm::run(rin, hb, lane, xrot + blk * kBlock);
+                }
+                uint4 xraw[4];
                 lds_barrier();
                 if (bid == 0 && op.x_rot)
                     for (int j = tid; j < nb * 128; j += kThreads)
@@ -412,13 +398,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
     }
 }
 
-// LDS below the partial sums: rotated input, then the images and records,
-// which first hold the rotation's transpose scratch
-int64_t lds_need(int64_t nb) {
-    const int64_t tail = nb * kImgBlock + nb * 4 * kRecBytes;
-    const int64_t scratch = nb * rot::kScratchBytes;
-    return nb * 2048 + (tail > scratch ? tail : scratch);
-}
+// LDS below the partial sums: rotated input, then the images and records
+int64_t lds_need(int64_t nb) { return nb * 2048 + nb * kImgBlock + nb * 4 * kRecBytes; }
 
 bool overlap(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
     if (!a || !b) return false;

@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     void* __restrict__ y, int y_f16) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int nb = int(k / kBlock);
-    // ROT: [rotated activations nb * 2 KB][transpose scratch, later the images ...]
+    // ROT: [rotated activations nb * 2 KB][images ...]
     uint16_t* xrot = reinterpret_cast<uint16_t*>(smem);
     uint8_t* img = ROT ? smem + nb * 2048 : smem;
     uint8_t* rec = img + nb * kImgBlock;
@@ -272,13 +272,18 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     // loads go out.
     uint4 xraw[4];
     if constexpr (ROT) {
-        uint4 sr[2];
-        rot::load(x, signs, nb, tid, xraw, sr);
+        // wave w rotates blocks w and w + kWaves (nb <= 32), stage 1 on the
+        // matrix cores
+        rotm::In rin[2];
+        rotm::load(x, signs, nb, wave, lane, rin[0]);
+        rotm::load(x, signs, nb, wave + kWaves, lane, rin[1]);
         set_chunk(0);
         issue(first, Zero{}, Head{});
         __builtin_amdgcn_sched_barrier(0);   // the rotation stays below those weight loads
-        rot::run(xraw, sr, nb, tid, reinterpret_cast<float*>(img), rot::kScratchFloats, xrot,
-                 kBlock);   // nb <= 32 half-waves
+        rotm::half8v hb[2];
+        rotm::h_operand(lane, hb);
+        if (wave < nb) rotm::run(rin[0], hb, lane, xrot + wave * kBlock);
+        if (wave + kWaves < nb) rotm::run(rin[1], hb, lane, xrot + (wave + kWaves) * kBlock);
         lds_barrier();
         if (blockIdx.x == 0)
             for (int i = tid; i < nb * 128; i += kThreads)
@@ -365,8 +370,7 @@ M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     p.rpc = int(rpc);
     p.steps = int(((rpc + 3) / 4 * nb + kWaves - 1) / kWaves);   // units of 4 rows per wave
     const size_t tail = size_t(nb) * kImgBlock + size_t(nb) * 4 * kRecBytes + size_t(rpc * nb) * 16;
-    const size_t scratch = size_t(nb) * rot::kScratchBytes;
-    p.lds = rot ? size_t(nb) * 2048 + (tail > scratch ? tail : scratch) : tail;
+    p.lds = rot ? size_t(nb) * 2048 + tail : tail;   // ROT: the rotated activations first
     return p;
 }
 
