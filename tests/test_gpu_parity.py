@@ -313,9 +313,9 @@ def _rotation_bound_ok(got, want, x16, roundings=10):
 @pytest.mark.parametrize("m,n,k", [(1, 1024, 1024), (1, 333, 5120), (1, 2048, 17408),
                                    (1, 300, 24576), (3, 700, 2048), (70, 200, 3072)])
 def test_linear_matches_oracle(gpu, fmt, m, n, k):
-    """M = 1 runs the fused kernels (rotation in the GEMV's prologue) except
-    dense trits at K = 24576, whose rotation slots do not fit in LDS beside the
-    decode table: there the rotation and the GEMV are two launches."""
+    """M = 1 runs the fused kernels (rotation in the GEMV's prologue, its first
+    stage on the matrix cores); M > 1 the rotation and the product as two
+    launches."""
     inp = synth.linear_inputs(n, k, m, cfg=3, linear=m + n + k, outliers=True)
     packed = tl.pack(dev(inp.codes, gpu), fmt)
     scales = dev(inp.scales, gpu)
@@ -325,7 +325,7 @@ def test_linear_matches_oracle(gpu, fmt, m, n, k):
     xr = host(x_rot)
     # the rotated activations it wrote: the rotation's own bound
     assert _rotation_bound_ok(xr.astype(np.float64), oracle.rotate(inp.x, inp.signs), inp.x,
-                              roundings=37 if fmt == tl.FMT_SLOT2 and m == 1 else 10)
+                              roundings=37 if m == 1 else 10)
     # the product is exactly the library's product on those activations
     prod = tl.gemm if m >= 64 else tl.gemv
     y2 = host(prod(packed, scales, fmt, x_rot)).astype(np.float64)
@@ -335,13 +335,16 @@ def test_linear_matches_oracle(gpu, fmt, m, n, k):
 
 
 @pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
-@pytest.mark.parametrize("n,k", [(1, 1024), (17, 2048), (1, 18432), (4097, 1024)])
+@pytest.mark.parametrize("n,k", [(1, 1024), (17, 2048), (1, 18432), (1, 46080), (4097, 1024)])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.float16], ids=["f32", "f16"])
 def test_linear_fused_plan_edges(gpu, fmt, n, k, out_dtype):
     """The fused M = 1 kernels at the edges of their launch plans: one row
-    (one workgroup whose waves split K), a ragged row tile, 18 blocks (the
-    largest K at which the dense-trit rotation slots fit for every N) and a
-    ragged last row slice; fp32 and binary16 outputs.  The product equals the
+    (one workgroup whose waves split K), a ragged row tile, 18 blocks, 45
+    blocks (the largest K at which the dense-trit kernel's rotated
+    activations fit in LDS beside its table: its waves rotate up to three
+    blocks each; the 2-bit kernels take 32 blocks at most, so there the
+    rotation and the product are two launches) and a ragged last row slice;
+    fp32 and binary16 outputs.  The product equals the
     library's GEMV on the x_rot the call wrote, bit for bit, and the layer
     meets the 2e-3 bar against the oracle."""
     inp = synth.linear_inputs(n, k, 1, cfg=3, linear=n + k, outliers=True)
@@ -351,7 +354,7 @@ def test_linear_fused_plan_edges(gpu, fmt, n, k, out_dtype):
     y = host(tl.linear(packed, scales, fmt, dev(inp.x, gpu), dev(inp.signs, gpu),
                        out_dtype=out_dtype, x_rot=x_rot))
     assert _rotation_bound_ok(host(x_rot).astype(np.float64), oracle.rotate(inp.x, inp.signs), inp.x,
-                              roundings=37 if fmt == tl.FMT_SLOT2 else 10)
+                              roundings=37)
     y2 = host(tl.gemv(packed, scales, fmt, x_rot, out_dtype=out_dtype))
     assert np.array_equal(y.view(np.uint16 if out_dtype == torch.float16 else np.uint32),
                           y2.view(np.uint16 if out_dtype == torch.float16 else np.uint32))

@@ -265,9 +265,9 @@ __device__ __forceinline__ void flight_n(int nr, const uint8_t* wb, const uint16
 }
 
 // ROT (M = 1, activations in LDS): x holds the unrotated activations and
-// signs their signs; the workgroup rotates them into LDS first, one
-// rot::kScratchBytes slot per 1024-block (the block's transpose scratch, then
-// its 1024 binary16 values), and workgroup 0 also writes them to x_rot.
+// signs their signs; the workgroup rotates them into LDS first (the 2-bit
+// kernel's rotation: one wave per 1024-block, the first stage on the matrix
+// cores), and workgroup 0 also writes them to x_rot.
 template <int NT, bool XLDS, bool ROT>
 __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, const int8_t* signs,
@@ -306,24 +306,27 @@ __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
     // published before any weight load is issued.
     const uint32_t xs_lds =
         uint32_t(uintptr_t((__attribute__((address_space(3))) uint16_t*)(xs)));
-    const uint32_t xstride = ROT ? uint32_t(rot::kScratchBytes) : 2048u;   // per 1024-block
+    const uint32_t xstride = 2048u;   // per 1024-block
     const uint32_t zero_lds = xs_lds + uint32_t(m) * uint32_t(blocks) * xstride;   // 16-byte zero pad
     if constexpr (ROT) {
-        // the loads go out first, the table is built while they are in flight
-        uint4 xr[4], sr[2];
-        rot::load(x, signs, blocks, tid, xr, sr);
+        // the loads of a wave's first block go out first, the table is built
+        // while they are in flight; wave w rotates blocks w, w + nwaves, ...
+        rotm::In rin;
+        rotm::load(x, signs, blocks, wave, lane, rin);
         build_lut(lut, tid, nthreads);
         if (tid == 0)
             *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(zero_lds) =
                 u32x4{0, 0, 0, 0};
-        rot::run(xr, sr, blocks, tid, reinterpret_cast<float*>(xs), rot::kScratchFloats, xs,
-                 rot::kScratchBytes / 2);   // blocks * 32 <= nthreads (checked on the host)
+        rotm::half8v hb[2];
+        rotm::h_operand(lane, hb);
+        for (int blk = wave; blk < blocks; blk += nwaves) {
+            if (blk != wave) rotm::load(x, signs, blocks, blk, lane, rin);
+            rotm::run(rin, hb, lane, xs + blk * kBlock);
+        }
         vm_lds_barrier();
         if (blockIdx.x == 0)
             for (int i = tid; i < blocks * 128; i += nthreads)
-                reinterpret_cast<uint4*>(x_rot)[i] = *reinterpret_cast<const uint4*>(
-                    reinterpret_cast<const uint8_t*>(xs) + (i >> 7) * rot::kScratchBytes +
-                    (i & 127) * 16);
+                reinterpret_cast<uint4*>(x_rot)[i] = reinterpret_cast<const uint4*>(xs)[i];
     } else {
         if (XLDS) {
             const int pieces = int(int64_t(m) * k / 512);   // M*K is a multiple of 1024
@@ -441,12 +444,11 @@ Plan make_plan(int64_t n, int max_w) {
     return p;
 }
 
-// LDS bytes of a launch: table, reduction buffer, activations (one rotation
-// slot per 1024-block when the kernel rotates) and a 16-byte zero pad
-template <int NT, bool XLDS, bool ROT>
+// LDS bytes of a launch: table, reduction buffer, activations and a 16-byte
+// zero pad
+template <int NT, bool XLDS>
 constexpr int64_t lds_bytes(int mt, int64_t k) {
-    return kLutBytes + int64_t(waves<NT>()) * NT * 64 * 4 +
-           (XLDS ? (ROT ? (k / kBlock) * rot::kScratchBytes : int64_t(mt) * k * 2) + 16 : 0);
+    return kLutBytes + int64_t(waves<NT>()) * NT * 64 * 4 + (XLDS ? int64_t(mt) * k * 2 + 16 : 0);
 }
 
 template <int NT, bool XLDS, bool ROT = false>
@@ -456,7 +458,7 @@ hipError_t launch_one(const Plan& plan, const uint8_t* packed, const uint16_t* s
     const hipError_t e =
         allow_lds(reinterpret_cast<const void*>(gemv_trit5_kernel<NT, XLDS, ROT>), int(kLdsLimit));
     if (e != hipSuccess) return e;
-    size_t lds = size_t(lds_bytes<NT, XLDS, ROT>(mt, k));
+    size_t lds = size_t(lds_bytes<NT, XLDS>(mt, k));
     // ask for more than half of the CU's LDS so that two workgroups never share a CU
     if (lds < size_t(kLdsLimit / 2 + 1024)) lds = size_t(kLdsLimit / 2 + 1024);
     hipLaunchKernelGGL((gemv_trit5_kernel<NT, XLDS, ROT>), dim3(unsigned(plan.grid)),
@@ -481,13 +483,11 @@ hipError_t launch_nt(const uint8_t* packed, const uint16_t* scales, const uint16
 
 }  // namespace
 
-// tl_linear at M = 1 in one launch: every 1024-block needs a half-wave of the
-// workgroup for its rotation, and its slot must fit in LDS beside the table
+// tl_linear at M = 1 in one launch: the rotated activations must fit in LDS
+// beside the table
 bool linear_m1_trit5_fits(int64_t m, int64_t n, int64_t k) {
-    if (m != 1) return false;
-    const Plan plan = make_plan(n, waves<1>());
-    return (k / kBlock) * 32 <= int64_t(plan.waves) * 64 &&
-           lds_bytes<1, true, true>(1, k) <= kLdsLimit;
+    (void)n;
+    return m == 1 && lds_bytes<1, true>(1, k) <= kLdsLimit;
 }
 
 hipError_t launch_linear_m1_trit5(const uint8_t* packed, const uint16_t* scales,
