@@ -302,12 +302,12 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
             {
                 // one block's input in registers at a time: this kernel holds
                 // the next linear's first weight steps through the rotation
-                rotm::half8v hb[2];
-                rotm::h_operand(lane, hb);
+                rot::half8v hb[2];
+                rot::h_operand(lane, hb);
                 for (int blk = wave; blk < nb; blk += kWaves) {
-                    rotm::In rin;
-                    rotm::load<kDeviceScope>(op.x, op.signs, nb, blk, lane, rin);
-                    rotm::run(rin, hb, lane, xrot + blk * kBlock);
+                    rot::In rin;
+                    rot::load<kDeviceScope>(op.x, op.signs, nb, blk, lane, rin);
+                    rot::run(rin, hb, lane, xrot + blk * kBlock);
                 }
                 uint4 xraw[4];
                 lds_barrier();

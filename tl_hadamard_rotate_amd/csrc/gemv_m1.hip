@@ -274,16 +274,16 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     if constexpr (ROT) {
         // wave w rotates blocks w and w + kWaves (nb <= 32), stage 1 on the
         // matrix cores
-        rotm::In rin[2];
-        rotm::load(x, signs, nb, wave, lane, rin[0]);
-        rotm::load(x, signs, nb, wave + kWaves, lane, rin[1]);
+        rot::In rin[2];
+        rot::load(x, signs, nb, wave, lane, rin[0]);
+        rot::load(x, signs, nb, wave + kWaves, lane, rin[1]);
         set_chunk(0);
         issue(first, Zero{}, Head{});
         __builtin_amdgcn_sched_barrier(0);   // the rotation stays below those weight loads
-        rotm::half8v hb[2];
-        rotm::h_operand(lane, hb);
-        if (wave < nb) rotm::run(rin[0], hb, lane, xrot + wave * kBlock);
-        if (wave + kWaves < nb) rotm::run(rin[1], hb, lane, xrot + (wave + kWaves) * kBlock);
+        rot::half8v hb[2];
+        rot::h_operand(lane, hb);
+        if (wave < nb) rot::run(rin[0], hb, lane, xrot + wave * kBlock);
+        if (wave + kWaves < nb) rot::run(rin[1], hb, lane, xrot + (wave + kWaves) * kBlock);
         lds_barrier();
         if (blockIdx.x == 0)
             for (int i = tid; i < nb * 128; i += kThreads)
@@ -416,7 +416,7 @@ bool m1_fits(int64_t m, int64_t n, int64_t k, bool rot) {
     const int64_t nb = k / kBlock;
     const int64_t grid = n < cu_count() ? n : cu_count();
     const int64_t rows = (n + grid - 1) / grid;
-    // one image pass (32 threads per block, one half-wave per rotated block)
+    // one image pass (32 threads per block)
     // and 32-bit buffer offsets
     return m == 1 && nb * 32 <= kThreads && m1_plan(n, k, rot).lds <= kLdsLimit &&
            rows * (k / 4) < (int64_t(1) << 31);

@@ -311,17 +311,17 @@ __global__ __launch_bounds__(64 * waves<NT>()) void gemv_trit5_kernel(
     if constexpr (ROT) {
         // the loads of a wave's first block go out first, the table is built
         // while they are in flight; wave w rotates blocks w, w + nwaves, ...
-        rotm::In rin;
-        rotm::load(x, signs, blocks, wave, lane, rin);
+        rot::In rin;
+        rot::load(x, signs, blocks, wave, lane, rin);
         build_lut(lut, tid, nthreads);
         if (tid == 0)
             *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(zero_lds) =
                 u32x4{0, 0, 0, 0};
-        rotm::half8v hb[2];
-        rotm::h_operand(lane, hb);
+        rot::half8v hb[2];
+        rot::h_operand(lane, hb);
         for (int blk = wave; blk < blocks; blk += nwaves) {
-            if (blk != wave) rotm::load(x, signs, blocks, blk, lane, rin);
-            rotm::run(rin, hb, lane, xs + blk * kBlock);
+            if (blk != wave) rot::load(x, signs, blocks, blk, lane, rin);
+            rot::run(rin, hb, lane, xs + blk * kBlock);
         }
         vm_lds_barrier();
         if (blockIdx.x == 0)
