@@ -584,7 +584,7 @@ def profile_pass(torch, tl, synth, dev, fmt) -> int:
     torch.cuda.synchronize()
     del src, dst
     if fmt in (0, 1):
-        steps, _ = build_mlp_step(torch, tl, synth, dev, 8, fmt)
+        steps, _, _ = build_mlp_step(torch, tl, synth, dev, 8, fmt)
         for i in range(10):
             for fn in steps[i % 8]:
                 fn()
@@ -736,7 +736,8 @@ def build_mlp_step(torch, tl, synth, dev, copies, fmt=1):
     binary16 output) then down on the gate part of that output (the SwiGLU
     between them in a model is outside this library; stream order makes down
     wait for gate|up), with packing fmt.  Returns per-copy lists of the two
-    launches (callables) and the step's algorithmic bytes."""
+    launches (callables), the step's algorithmic bytes and what the output
+    checks read (the step's buffers and host inputs)."""
     import numpy as np
 
     ins = {}
@@ -768,7 +769,46 @@ def build_mlp_step(torch, tl, synth, dev, copies, fmt=1):
             (lambda pd=pd, sd=sd: tl.linear(pd, sd, fmt, x_dn, s_dn, out=y_dn, x_rot=xr_dn))])
     launch_bytes = [linear_bytes(2 * ng, kg, 1, fmt) - 2 * ng * 2,    # binary16 output
                     linear_bytes(nd, kd, 1, fmt)]
-    return steps, launch_bytes
+    io = dict(fmt=fmt, gu_packed=gu_packed, gu_scales=gu_scales, dn_packed=dn_packed,
+              dn_scales=dn_scales, y_gu=y_gu, y_dn=y_dn, xr_gu=xr_gu, xr_dn=xr_dn, g=g, u=u, d=d,
+              kd=kd)
+    return steps, launch_bytes, io
+
+
+def check_step_outputs(torch, tl, io):
+    """After the timed steps: the step's outputs are finite and equal, bit for
+    bit, the library's GEMV on the x_rot the fused launches wrote (one
+    launch per linear, outside the timed region)."""
+    y_gu = tl.gemv(io["gu_packed"], io["gu_scales"], io["fmt"], io["xr_gu"], out_dtype=torch.float16)
+    y_dn = tl.gemv(io["dn_packed"], io["dn_scales"], io["fmt"], io["xr_dn"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(y_gu.view(torch.int16), io["y_gu"].view(torch.int16)) and
+                torch.equal(y_dn.view(torch.int32), io["y_dn"].view(torch.int32)))
+    finite = bool(torch.isfinite(io["y_gu"].float()).all().item() and
+                  torch.isfinite(io["y_dn"]).all().item())
+    io["y_gu_host"] = io["y_gu"].cpu().numpy()
+    io["y_dn_host"] = io["y_dn"].cpu().numpy()
+    return {"finite": finite, "equal_to_gemv_on_x_rot": same}
+
+
+def oracle_check_step(oracle, io, rows=32):
+    """Sampled rows of the step's outputs against the oracle's layer (fp64
+    rotation and product; down on the binary16 gate|up output the step
+    produced): relative L2 errors, to compare with the 2e-3 bar."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    g, u, d, kd = io["g"], io["u"], io["d"], io["kd"]
+    codes_gu = np.concatenate([g.codes, u.codes])
+    scales_gu = np.concatenate([g.scales, u.scales])
+    y_gu, y_dn = io["y_gu_host"], io["y_dn_host"]
+    r1 = rng.choice(codes_gu.shape[0], size=rows, replace=False)
+    r2 = rng.choice(d.codes.shape[0], size=rows, replace=False)
+    want_gu = oracle.linear(g.x, g.signs, codes_gu[r1], scales_gu[r1])
+    want_dn = oracle.linear(y_gu[:, :kd], d.signs, d.codes[r2], d.scales[r2])
+    return {"rows_per_linear": rows,
+            "rel_l2_gate_up": float(oracle.rel_l2(y_gu[:, r1].astype(np.float64), want_gu)),
+            "rel_l2_down": float(oracle.rel_l2(y_dn[:, r2].astype(np.float64), want_dn)),
+            "bar": 2e-3}
 
 
 def per_launch_times_us(torch, steps, reps, stream):
@@ -958,7 +998,7 @@ def main(argv=None) -> int:
     extra = {}
     # the step: gate|up then down, two fused rotate + GEMV launches
     log(f"building the step (gate|up, down), fmt={args.fmt}, copies={args.copies}")
-    steps, launch_bytes = build_mlp_step(torch, tl, synth, dev, args.copies, fmt)
+    steps, launch_bytes, step_io = build_mlp_step(torch, tl, synth, dev, args.copies, fmt)
     with torch.cuda.stream(stream):
         step_graphs = capture(torch, lambda c: [fn() for fn in steps[c]], args.copies, stream)
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
@@ -966,6 +1006,9 @@ def main(argv=None) -> int:
     sbytes = sum(launch_bytes)
     launches = 2
     per = per_launch_times_us(torch, steps, max(args.steps, 2 * args.copies), stream)
+    extra["output_check"] = check_step_outputs(torch, tl, step_io)
+    for key in ("gu_packed", "gu_scales", "dn_packed", "dn_scales", "y_gu", "y_dn", "xr_gu", "xr_dn"):
+        del step_io[key]
     kern_us = sum(per) / len(per)
     per_launch = sbytes / len(per)
     kname = ("gemv_m1_slot2_kernel<FL, true> (tl_linear, rotation fused): gate|up and down"
@@ -1037,7 +1080,7 @@ def main(argv=None) -> int:
         other = 1 - fmt
         oname = "slot2" if other == 1 else "trit5"
         log(f"the step (gate|up, down) with fmt={oname}")
-        steps2, lb2 = build_mlp_step(torch, tl, synth, dev, args.copies, other)
+        steps2, lb2, _ = build_mlp_step(torch, tl, synth, dev, args.copies, other)
         with torch.cuda.stream(stream):
             sg2 = capture(torch, lambda c: [fn() for fn in steps2[c]], args.copies, stream)
         ms3 = timed_replays(torch, sg2, args.steps, args.warmup, stream) / args.steps
@@ -1092,6 +1135,8 @@ def main(argv=None) -> int:
         import oracle   # the checker, timed as the CPU baseline; the GPU path never uses it
         log("timing the CPU oracle sample")
         cpu = cpu_baseline(oracle, synth, fmt)
+        log("sampled rows of the step's outputs against the oracle")
+        extra["output_check"].update(oracle_check_step(oracle, step_io))
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
