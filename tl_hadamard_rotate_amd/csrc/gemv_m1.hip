@@ -59,6 +59,9 @@ using namespace m1;
 
 constexpr int kRingFlights = 3;   // flights of a chunk streamed as a ring: up to 4 in all
 constexpr int kRingMaxFL = 6;     // flight length of the ring (8 does not fit the registers)
+// cache policy of the weight and scale loads: read once per call, streamed
+// (nontemporal) so that they do not push the activations out of the caches
+constexpr int kNonTemporal = 2;
 
 // ROT: x is the unrotated activations and signs their signs; the workgroup
 // rotates them in LDS first, and workgroup 0 also writes them to x_rot.
@@ -171,9 +174,9 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         const int r0e = row0(e);
         const int r = rc0 + r0e;
         wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              wsrc, w_lane, uint32_t(r * int(row_bytes) + 256 * e.b), 0));
+                                              wsrc, w_lane, uint32_t(r * int(row_bytes) + 256 * e.b), kNonTemporal));
         sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, s_lane,
-                                                     uint32_t((r * int(groups) + 8 * e.b) * 2), 0);
+                                                     uint32_t((r * int(groups) + 8 * e.b) * 2), kNonTemporal);
         sb[t] = e.b;
         sro[t] = (r0e * nb + e.b) * 4;
     };
