@@ -97,6 +97,9 @@ __device__ __forceinline__ uint32_t ld_agent(const uint32_t* p) {
 // read as a later linear's input): coherent at device scope (sc1), so no
 // cache has to be written back or invalidated for them.
 constexpr int kDeviceScope = 16;
+// Cache policy of the weight and scale loads: read once per chain, streamed
+// (nontemporal) so that they do not push the linears' inputs out of the caches.
+constexpr int kNonTemporal = 2;
 
 // s_waitcnt immediate: vector memory count 0, the other counters not waited
 constexpr int kVmcntZero = 0x0F70;
@@ -181,8 +184,8 @@ __global__ __launch_bounds__(kThreads) void chain_kernel(const uint8_t* __restri
         const bool ok = want && l.live && l.f0 + t < l.end;
         const uint32_t wo = ok ? uint32_t(l.r * l.row_bytes + 256 * l.b + 16 * u) : kOob;
         const uint32_t so = ok ? uint32_t((l.r * l.groups + 8 * l.b + 2 * ip) * 2) : kOob;
-        wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(l.wsrc, wo, 0, 0));
-        sv[t] = __builtin_amdgcn_raw_buffer_load_b32(l.ssrc, so, 0, 0);
+        wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(l.wsrc, wo, 0, kNonTemporal));
+        sv[t] = __builtin_amdgcn_raw_buffer_load_b32(l.ssrc, so, 0, kNonTemporal);
         // keep the loads in step order: the compiler then waits for exactly
         // the step it consumes (else it hoists the refills above the steps
         // and waits for every load in flight)
