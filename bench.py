@@ -296,12 +296,25 @@ def bench_batched(torch, tl, synth, dev, fmt, copies=20):
     """Batched decode GEMV over one layer's attention projections q, k, v, o
     at M in {1, 2, 4, 8, 16} (activations with 1% outliers x20); weights
     cycled over `copies` distinct buffers (> the last-level cache), the
-    launches captured in one HIP graph (launch time per GEMV, gaps included)."""
+    launches captured in one HIP graph (launch time per GEMV, gaps included);
+    also q|k|v, the three projections that read one input with their rows
+    concatenated, as one launch."""
+    import dataclasses
+
+    import numpy as np
     out = []
+    ins = {}
     for name in ("q", "k", "v", "o"):
         k, n = synth.SHAPES[name]
-        inp = synth.linear_inputs(n, k, 16, seed=0, cfg=3, linear=synth.LINEAR_ID[name],
-                                  outliers=True)
+        ins[name] = synth.linear_inputs(n, k, 16, seed=0, cfg=3, linear=synth.LINEAR_ID[name],
+                                        outliers=True)
+    # q, k and v read the same input: their rows concatenated along N run as
+    # one launch (q's activations and signs)
+    qkv = dataclasses.replace(ins["q"], codes=np.concatenate([ins[c].codes for c in "qkv"]),
+                              scales=np.concatenate([ins[c].scales for c in "qkv"]))
+    for name, inp in (("q", ins["q"]), ("k", ins["k"]), ("v", ins["v"]), ("o", ins["o"]),
+                      ("q|k|v", qkv)):
+        n, k = inp.codes.shape
         packed = tl.pack(torch.from_numpy(inp.codes).to(dev), fmt)
         scales = torch.from_numpy(inp.scales).to(dev)
         packs = [packed] + [packed.clone() for _ in range(copies - 1)]

@@ -178,6 +178,42 @@ def test_batched_decode_full_size(gpu, shape, fmt):
             assert np.array_equal(yh.view(np.uint16), y.astype(np.float16).view(np.uint16))
 
 
+@pytest.mark.parametrize("fmt", FMTS, ids=FMT_NAME.get)
+def test_batched_decode_qkv_concatenated(gpu, fmt):
+    """q, k and v read one input, so their rows concatenated along N run as
+    one tl_linear (one rotation, one launch) at M = 1, 2, 4, 8, 16: every
+    token on sampled rows of each part against the oracle, and each part
+    equal to that projection's own call (bit for bit with 2-bit slots, whose
+    rows do not depend on the other rows of the launch; to fp32 rounding
+    with dense trits, whose K split follows the rows per CU)."""
+    ins = {c: _inputs(c, 16, 3, True) for c in "qkv"}
+    codes = np.concatenate([ins[c].codes for c in "qkv"])
+    scales = np.concatenate([ins[c].scales for c in "qkv"])
+    bounds = np.cumsum([0] + [ins[c].codes.shape[0] for c in "qkv"])
+    x, signs = ins["q"].x, ins["q"].signs
+    packed = tl.pack(dev(codes, gpu), fmt)
+    sc = dev(scales, gpu)
+    parts = {c: (tl.pack(dev(ins[c].codes, gpu), fmt), dev(ins[c].scales, gpu)) for c in "qkv"}
+    rng = np.random.default_rng(7)
+    for m in synth.BATCHED_M:
+        xm, sg = dev(x[:m], gpu), dev(signs, gpu)
+        x_rot = torch.empty((m, x.shape[1]), dtype=torch.float16, device=gpu)
+        y = host(tl.linear(packed, sc, fmt, xm, sg, x_rot=x_rot))
+        xr = host(x_rot)
+        for i, c in enumerate("qkv"):
+            r0, r1 = bounds[i], bounds[i + 1]
+            yc = y[:, r0:r1]
+            own = host(tl.linear(parts[c][0], parts[c][1], fmt, xm, sg))
+            if fmt == tl.FMT_SLOT2:
+                assert np.array_equal(yc.view(np.uint32), own.view(np.uint32)), (m, c)
+            else:
+                assert oracle.rel_l2(yc, own) < 1e-6, (m, c)
+            sub = type(ins[c])(signs=signs, codes=ins[c].codes, scales=ins[c].scales, x=x[:m])
+            rows = tile_samples(r1 - r0, 64, rng)
+            e16, e = _check_sampled(yc, sub, xr, np.arange(m), rows)
+            assert e16 < 1e-5 and e < 2e-3, (m, c, e16, e)
+
+
 # ---------------------------------------------------------------------------
 # fused M = 1 path on the o projection, and a captured layer
 # ---------------------------------------------------------------------------
