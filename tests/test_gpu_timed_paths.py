@@ -183,9 +183,11 @@ def test_batched_decode_qkv_concatenated(gpu, fmt):
     """q, k and v read one input, so their rows concatenated along N run as
     one tl_linear (one rotation, one launch) at M = 1, 2, 4, 8, 16: every
     token on sampled rows of each part against the oracle, and each part
-    equal to that projection's own call (bit for bit with 2-bit slots, whose
-    rows do not depend on the other rows of the launch; to fp32 rounding
-    with dense trits, whose K split follows the rows per CU)."""
+    equal to that projection's own call to fp32 rounding (a launch's plan
+    follows its rows: with dense trits the K split, with 2-bit slots at
+    M = 5..8 the token groups, one of 8 or two of 4, which sum the digit
+    offsets in different orders), bit for bit for q with 2-bit slots, whose
+    own launch has the plan of q|k|v."""
     ins = {c: _inputs(c, 16, 3, True) for c in "qkv"}
     codes = np.concatenate([ins[c].codes for c in "qkv"])
     scales = np.concatenate([ins[c].scales for c in "qkv"])
@@ -204,10 +206,9 @@ def test_batched_decode_qkv_concatenated(gpu, fmt):
             r0, r1 = bounds[i], bounds[i + 1]
             yc = y[:, r0:r1]
             own = host(tl.linear(parts[c][0], parts[c][1], fmt, xm, sg))
-            if fmt == tl.FMT_SLOT2:
+            if fmt == tl.FMT_SLOT2 and c == "q":
                 assert np.array_equal(yc.view(np.uint32), own.view(np.uint32)), (m, c)
-            else:
-                assert oracle.rel_l2(yc, own) < 1e-6, (m, c)
+            assert oracle.rel_l2(yc, own) < 1e-6, (m, c)
             sub = type(ins[c])(signs=signs, codes=ins[c].codes, scales=ins[c].scales, x=x[:m])
             rows = tile_samples(r1 - r0, 64, rng)
             e16, e = _check_sampled(yc, sub, xr, np.arange(m), rows)

@@ -417,6 +417,21 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
     MtPlan p{};
     p.mt = pick_mt(m, k);
     if (p.mt == 0) return p;
+    // 5..8 tokens in one group of 8, or in two groups of 4 on paired
+    // workgroups (each reads the activations of 4 tokens and twice the rows):
+    // two groups when a workgroup of one group would read at least three
+    // times as many activation bytes (2 m K) as weight bytes (rows K / 4),
+    // i.e. rows <= 8 m / 3.  Measured at M = 8: k, v (N = 1024, 8 rows a
+    // workgroup) 5.7 -> 5.2 us and o (20 rows) 9.6 -> 8.9 us; q (24 rows)
+    // 7.75 -> 8.2 us and q|k|v (32 rows) 8.5 -> 9.1 us, so they keep one group.
+    if (p.mt == 8 && m > 4) {
+        const int64_t units1 = (n + kUnitRows - 1) / kUnitRows;
+        const int64_t sets1 = units1 < cu_count() ? units1 : cu_count();
+        const int64_t rows1 = (n + sets1 - 1) / sets1;
+        const bool four_fit = int64_t(4) * nb * 32 <= int64_t(rounds<4>()) * kThreads &&
+                              fixed_lds(nb, 4) + size_t(4 * nb) * 4 * 4 <= kLdsLimit;
+        if (3 * rows1 <= 8 * m && four_fit) p.mt = 4;
+    }
     p.groups = int((m + p.mt - 1) / p.mt);
     // at least a unit of rows per workgroup when there are few rows; with two
     // groups, half the CUs per group and the grid padded to whole 16s (the
