@@ -424,7 +424,7 @@ MtPlan mt_plan(int64_t m, int64_t n, int64_t k) {
     // i.e. rows <= 8 m / 3.  Measured at M = 8: k, v (N = 1024, 8 rows a
     // workgroup) 5.7 -> 5.2 us and o (20 rows) 9.6 -> 8.9 us; q (24 rows)
     // 7.75 -> 8.2 us and q|k|v (32 rows) 8.5 -> 9.1 us, so they keep one group.
-    if (p.mt == 8 && m > 4) {
+    if (p.mt == 8 && m > 4 && m <= 8) {
         const int64_t units1 = (n + kUnitRows - 1) / kUnitRows;
         const int64_t sets1 = units1 < cu_count() ? units1 : cu_count();
         const int64_t rows1 = (n + sets1 - 1) / sets1;
