@@ -114,3 +114,22 @@ def test_gemv_few_tokens_deterministic_and_token_independent(gpu):
         lone[1:] = 0
         c = host(tl.gemv(packed, scales, SLOT2, dev(lone, gpu)))
         assert np.array_equal(c[0].view(np.uint32), rand[0].view(np.uint32)), mm
+
+
+@pytest.mark.parametrize("shape", ["q", "gate"])
+def test_gemv_sixteen_tokens_are_two_groups_of_eight(gpu, shape):
+    """At M = 16 on q and gate the few-token kernel runs two groups of 8 tokens
+    in one launch, each with the arithmetic of an 8-token launch: tokens
+    0..7 and 8..15 equal, bit for bit, the launches on those 8 tokens alone
+    (a launch plan that sent M = 16 to another kernel would change the
+    rounding of the sums).  Both shapes take one group of 8 at M = 8: their
+    workgroups hold more than 8 M / 3 rows."""
+    k, n = synth.SHAPES[shape]
+    inp = synth.linear_inputs(n, k, 16, cfg=3, linear=synth.LINEAR_ID[shape], outliers=True)
+    packed = tl.pack(dev(inp.codes, gpu), SLOT2)
+    scales = dev(inp.scales, gpu)
+    x16 = oracle.rotate(inp.x, inp.signs).astype(np.float16)
+    y = host(tl.gemv(packed, scales, SLOT2, dev(x16, gpu)))
+    for g in range(2):
+        part = host(tl.gemv(packed, scales, SLOT2, dev(x16[8 * g:8 * g + 8], gpu)))
+        assert np.array_equal(y[8 * g:8 * g + 8].view(np.uint32), part.view(np.uint32)), g
