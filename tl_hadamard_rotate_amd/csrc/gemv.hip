@@ -15,6 +15,8 @@ hipError_t launch_gemv(const uint8_t* packed, const uint16_t* scales, int fmt, c
                 return launch_gemv_mt_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
             return launch_gemv_slot2(packed, scales, x, m, n, k, y, y_f16, stream);
         case 2:
+            if (gemv_m1_bit1_fits(m, n, k))
+                return launch_gemv_m1_bit1(packed, scales, x, n, k, y, y_f16, stream);
             if (gemv_mt_bit1_fits(m, n, k))
                 return launch_gemv_mt_bit1(packed, scales, x, m, n, k, y, y_f16, stream);
             return launch_gemv_bit1(packed, scales, x, m, n, k, y, y_f16, stream);

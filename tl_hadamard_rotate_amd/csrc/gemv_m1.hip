@@ -65,7 +65,12 @@ constexpr int kNonTemporal = 2;
 
 // ROT: x is the unrotated activations and signs their signs; the workgroup
 // rotates them in LDS first, and workgroup 0 also writes them to x_rot.
-template <int FL, bool ROT>
+// B1: the 1-bit packing (codes -1 and +1, bit b = (code + 1) / 2, 16 bytes
+// per 128 weights): a lane loads the 8 bytes that hold the 64 weights it
+// would read as 16 bytes of 2-bit slots, and each 16 bits of them are
+// spread into the 2-bit-slot word of the same weights (digit 2b = code + 1);
+// everything after that is the 2-bit-slot kernel.
+template <int FL, bool ROT, bool B1>
 __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     const uint8_t* packed, const uint16_t* scales, const uint16_t* x, const int8_t* signs,
     uint16_t* x_rot, int64_t k, int row_base, int row_rem, int rows_per_chunk,
@@ -92,7 +97,9 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     const int bid = int(blockIdx.x);
     const int64_t r0 = int64_t(bid) * row_base + min(bid, row_rem);
     const int rows = row_base + (bid < row_rem ? 1 : 0);
-    const int64_t row_bytes = k / 4;
+    const int64_t row_bytes = B1 ? k / 8 : k / 4;
+    constexpr int kLaneBytes = B1 ? 8 : 16;          // a lane's bytes of a step
+    constexpr int kSegBytes = 16 * kLaneBytes;       // a row's bytes of a 1024-block
     const int64_t groups = k / kGroup;
     const __amdgpu_buffer_rsrc_t wsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(packed + r0 * row_bytes), 0, int(rows * row_bytes), kRsrcWord3);
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
         first = cur_at(vb);
         flights = ((units + kWaves - 1) / kWaves + FL - 1) / FL;   // workgroup-uniform
         const int s_eff = min(slot_in_wave, rc - 1);
-        w_lane = uint32_t(s_eff * int(row_bytes) + 16 * u);
+        w_lane = uint32_t(s_eff * int(row_bytes) + kLaneBytes * u);
         s_lane = uint32_t((s_eff * int(groups) + 2 * ip) * 2);
         red_lane = s_eff * nb * 4 + ip;
     };
@@ -166,15 +173,19 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     // Step t of a flight: its weights and scales in registers, and (scalar)
     // its block and the offset of its partial sums in red, set when its loads
     // are issued so that consuming it takes no unit arithmetic.
-    uint4 wv[FL];
+    using WReg = std::conditional_t<B1, u32x2, uint4>;
+    WReg wv[FL];
     uint32_t sv[FL];
     int sb[FL], sro[FL];
     auto load_step = [&](int t, const Cur& c) {
         const Cur e = eff(c);
         const int r0e = row0(e);
         const int r = rc0 + r0e;
-        wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              wsrc, w_lane, uint32_t(r * int(row_bytes) + 256 * e.b), kNonTemporal));
+        const uint32_t wo = uint32_t(r * int(row_bytes) + kSegBytes * e.b);
+        if constexpr (B1)
+            wv[t] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(wsrc, w_lane, wo, kNonTemporal));
+        else
+            wv[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wsrc, w_lane, wo, kNonTemporal));
         sv[t] = __builtin_amdgcn_raw_buffer_load_b32(ssrc, s_lane,
                                                      uint32_t((r * int(groups) + 8 * e.b) * 2), kNonTemporal);
         sb[t] = e.b;
@@ -212,8 +223,14 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
                 ry = rv.z;
                 cur_b = b;
             }
-            const auto p01 = __builtin_amdgcn_permlane32_swap(wv[t].x, wv[t].y, false, false);
-            const auto p23 = __builtin_amdgcn_permlane32_swap(wv[t].z, wv[t].w, false, false);
+            uint4 w4;
+            if constexpr (B1)
+                w4 = uint4{spread_bits(wv[t][0], 0), spread_bits(wv[t][0], 1),
+                           spread_bits(wv[t][1], 0), spread_bits(wv[t][1], 1)};
+            else
+                w4 = wv[t];
+            const auto p01 = __builtin_amdgcn_permlane32_swap(w4.x, w4.y, false, false);
+            const auto p23 = __builtin_amdgcn_permlane32_swap(w4.z, w4.w, false, false);
             float4v dx = float4v{0.0f, 0.0f, 0.0f, 0.0f};
             float4v dy = float4v{0.0f, 0.0f, 0.0f, 0.0f};
             dx = mac_eword(p01[0], a[0], a[1], dx);
@@ -341,15 +358,15 @@ __global__ __launch_bounds__(kThreads) void gemv_m1_slot2_kernel(
     }
 }
 
-template <int FL, bool ROT>
+template <int FL, bool ROT, bool B1>
 hipError_t launch_fl(unsigned grid, size_t lds, const uint8_t* packed, const uint16_t* scales,
                      const uint16_t* x, const int8_t* signs, uint16_t* x_rot, int64_t n,
                      int64_t k, int rpc, void* y, int y_f16, hipStream_t stream) {
     const int base = int(n / grid), rem = int(n % grid);
     const hipError_t e =
-        allow_lds(reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL, ROT>), int(kLdsLimit));
+        allow_lds(reinterpret_cast<const void*>(gemv_m1_slot2_kernel<FL, ROT, B1>), int(kLdsLimit));
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemv_m1_slot2_kernel<FL, ROT>), dim3(grid), dim3(kThreads), lds, stream,
+    hipLaunchKernelGGL((gemv_m1_slot2_kernel<FL, ROT, B1>), dim3(grid), dim3(kThreads), lds, stream,
                        packed, scales, x, signs, x_rot, k, base, rem, rpc, y, y_f16);
     return hipGetLastError();
 }
@@ -377,7 +394,7 @@ M1Plan m1_plan(int64_t n, int64_t k, bool rot) {
     return p;
 }
 
-template <bool ROT>
+template <bool ROT, bool B1>
 hipError_t launch_m1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                      const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k, void* y, int y_f16,
                      hipStream_t stream) {
@@ -385,37 +402,37 @@ hipError_t launch_m1(const uint8_t* packed, const uint16_t* scales, const uint16
     // up to 8 steps a slot: one flight, every load issued at once; up to
     // 4 flights of kRingMaxFL: a ring; beyond, flights of 8
     if (p.steps > 8 && p.steps <= kRingMaxFL * (kRingFlights + 1))
-        return launch_fl<kRingMaxFL, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k,
+        return launch_fl<kRingMaxFL, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k,
                                           p.rpc, y, y_f16, stream);
     switch (p.steps) {
         case 1:
-            return launch_fl<1, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<1, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 2:
-            return launch_fl<2, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<2, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 3:
-            return launch_fl<3, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<3, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 4:
-            return launch_fl<4, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<4, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 5:
-            return launch_fl<5, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<5, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 6:
-            return launch_fl<6, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<6, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         case 7:
-            return launch_fl<7, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<7, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
         default:
-            return launch_fl<8, ROT>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
+            return launch_fl<8, ROT, B1>(p.grid, p.lds, packed, scales, x, signs, x_rot, n, k, p.rpc, y,
                                      y_f16, stream);
     }
 }
 
-bool m1_fits(int64_t m, int64_t n, int64_t k, bool rot) {
+bool m1_fits(int64_t m, int64_t n, int64_t k, bool rot) {   // both packings
     const int64_t nb = k / kBlock;
     const int64_t grid = n < cu_count() ? n : cu_count();
     const int64_t rows = (n + grid - 1) / grid;
@@ -431,7 +448,7 @@ bool gemv_m1_slot2_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, 
 
 hipError_t launch_gemv_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                 int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
-    return launch_m1<false>(packed, scales, x, nullptr, nullptr, n, k, y, y_f16, stream);
+    return launch_m1<false, false>(packed, scales, x, nullptr, nullptr, n, k, y, y_f16, stream);
 }
 
 bool linear_m1_slot2_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, k, true); }
@@ -439,7 +456,22 @@ bool linear_m1_slot2_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n
 hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                   const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
                                   void* y, int y_f16, hipStream_t stream) {
-    return launch_m1<true>(packed, scales, x, signs, x_rot, n, k, y, y_f16, stream);
+    return launch_m1<true, false>(packed, scales, x, signs, x_rot, n, k, y, y_f16, stream);
+}
+
+bool gemv_m1_bit1_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, k, false); }
+
+hipError_t launch_gemv_m1_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                               int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream) {
+    return launch_m1<false, true>(packed, scales, x, nullptr, nullptr, n, k, y, y_f16, stream);
+}
+
+bool linear_m1_bit1_fits(int64_t m, int64_t n, int64_t k) { return m1_fits(m, n, k, true); }
+
+hipError_t launch_linear_m1_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                 const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
+                                 void* y, int y_f16, hipStream_t stream) {
+    return launch_m1<true, true>(packed, scales, x, signs, x_rot, n, k, y, y_f16, stream);
 }
 
 }  // namespace tl

@@ -65,7 +65,6 @@ namespace {
 
 using namespace m1;
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kUnitRows = 8;                 // rows of a unit (columns of a slot)
 constexpr uint32_t kOnes = 0x55555555u;      // 16 digits 1 (codes 0)
@@ -79,16 +78,6 @@ constexpr int rounds() { return MT == 2 ? 3 : 2; }
 
 __host__ __device__ constexpr int tok_stride(int nb) { return nb * kImgBlock + kTokPad; }
 __host__ __device__ constexpr int rec_tok_bytes(int nb) { return nb * 4 * kRecBytes; }
-
-// 16 bits of 1-bit codes (bits 16h .. 16h + 15 of w) as the 2-bit-slot word of
-// the same 16 weights: bit i moves to bit 2i + 1 (digit 2b)
-__device__ __forceinline__ uint32_t spread_bits(uint32_t w, int h) {
-    uint32_t v = __builtin_amdgcn_perm(0u, w, h ? 0x0C030C02u : 0x0C010C00u);   // byte per 16 bits
-    v = (v | (v << 4)) & 0x0F0F0F0Fu;
-    v = (v | (v << 2)) & 0x33333333u;
-    v = (v | (v << 1)) & 0x55555555u;
-    return v << 1;
-}
 
 template <int FL, int MT, bool B1>
 __global__ __launch_bounds__(kThreads) void gemv_mt_slot2_kernel(

@@ -15,6 +15,7 @@ namespace m1 {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -228,6 +229,16 @@ __device__ __forceinline__ float4v mac_eword(uint32_t e, const half8& a_lo, cons
     const half8 b_hi = as_h8(e & 0x03000300u, r6 & 0x00300030u, r6 & 0x00C000C0u, r6 & 0x03000300u);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_lo, b_lo, acc, 0, 0, 0);
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a_hi, b_hi, acc, 0, 0, 0);
+}
+
+// 16 bits of 1-bit codes (bits 16h .. 16h + 15 of w) as the 2-bit-slot word of
+// the same 16 weights: bit i moves to bit 2i + 1 (digit 2b)
+__device__ __forceinline__ uint32_t spread_bits(uint32_t w, int h) {
+    uint32_t v = __builtin_amdgcn_perm(0u, w, h ? 0x0C030C02u : 0x0C010C00u);   // byte per 16 bits
+    v = (v | (v << 4)) & 0x0F0F0F0Fu;
+    v = (v | (v << 2)) & 0x33333333u;
+    v = (v | (v << 1)) & 0x55555555u;
+    return v << 1;
 }
 
 __device__ __forceinline__ float pick(const float4v& d, int r) {

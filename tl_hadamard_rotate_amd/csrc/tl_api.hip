@@ -278,6 +278,9 @@ tl_status tl_linear(const uint8_t* packed, const uint16_t* scales, int32_t fmt, 
     if (fmt == TL_FMT_SLOT2 && tl::linear_m1_slot2_fits(M, N, K))
         return launched(
             tl::launch_linear_m1_slot2(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
+    if (fmt == TL_FMT_BIT1 && tl::linear_m1_bit1_fits(M, N, K))
+        return launched(
+            tl::launch_linear_m1_bit1(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));
     if (fmt == TL_FMT_TRIT5 && tl::linear_m1_trit5_fits(M, N, K))
         return launched(
             tl::launch_linear_m1_trit5(packed, scales, x, signs, x_rot, N, K, y, y_f16, stream));

@@ -42,6 +42,15 @@ bool linear_m1_slot2_fits(int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear_m1_slot2(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
                                   const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
                                   void* y, int y_f16, hipStream_t stream);
+// The same two for the 1-bit packing (each 16 bits spread into the 2-bit-slot
+// word of the same weights)
+bool gemv_m1_bit1_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemv_m1_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                               int64_t n, int64_t k, void* y, int y_f16, hipStream_t stream);
+bool linear_m1_bit1_fits(int64_t m, int64_t n, int64_t k);
+hipError_t launch_linear_m1_bit1(const uint8_t* packed, const uint16_t* scales, const uint16_t* x,
+                                 const int8_t* signs, uint16_t* x_rot, int64_t n, int64_t k,
+                                 void* y, int y_f16, hipStream_t stream);
 // 2 <= M <= 16 decode GEMV of the 2-bit-slot packing (tokens on the
 // matrix-core rows, up to 8 per workgroup, two token groups in one launch);
 // usable when gemv_mt_slot2_fits(m, n, k)
